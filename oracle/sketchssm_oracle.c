@@ -1,0 +1,398 @@
+/*
+ * SketchSSM decode oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU implementation of what the SketchSSM decode path
+ * computes, one (sequence, head) tile at a time.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header or constant with the HIP library and never calls it.
+ *
+ * Sources (the SketchSSM project page, arXiv 2609.33051 and its summaries):
+ *  - recurrence S_t = M_t S_{t-1} + B_t, read o_t = S_t^T q_t
+ *      (project page, "01 / The idea", full-state equation);
+ *  - flush: apply the buffered updates to the full state, then build the
+ *    sketch U = S^T Omega from the updated state; the flush step's own output
+ *    is computed from the updated state (paper App. B "SketchSSM algorithm";
+ *    project page "02 / How to make a sketch", per-window flush panel);
+ *  - non-flush read: c_t = C q~_t, o^_t = U c_t, plus the exact contribution
+ *    of the buffered updates (project page, per-step non-flush panel;
+ *    paper App. D);
+ *  - effective query q~_t: the query pulled back through the buffered
+ *    transitions, so that the state-read term is S_0^T q~_t (paper Sec. 3.2,
+ *    project page error objective; Mamba-2 has decay only, App. C.1);
+ *  - ReplaySSM: buffered writes, full-state read each step (paper Sec. 1-2,
+ *    App. D).
+ *
+ * Per family (readings where the pages are silent are listed in the design doc):
+ *   Mamba-2: M = a I, a = exp(-dt * exp(A_h)), B = dt k v^T
+ *   GDN:     M = alpha (I - beta k k^T),        B = beta k v^T
+ *   KDA:     M = (I - beta k k^T) Diag(g),      B = beta k v^T
+ *
+ * All arithmetic is fp64.  Values are rounded only where the method stores
+ * them: the state S (fp32), the sketch U (fp32 or bf16, via fp32, nearest
+ * even) and the output o (activation dtype).  The EXACT store mode keeps
+ * fp64 everywhere, for the algebraic pins.
+ *
+ * A mutation switch plants known mistakes so that a test can show the pins
+ * catch them; it is off (0) unless a test sets it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_MAMBA2 = 0, ORC_GDN = 1, ORC_KDA = 2 };
+enum { ORC_STORE_EXACT = 0, ORC_STORE_F32 = 1, ORC_STORE_BF16 = 2 };
+enum { ORC_OK = 0, ORC_ERR_COUNT = 1 };
+
+typedef struct {
+    int family;
+    int dk, dv, W;
+    int rmax;          /* row stride of U, Pt, C */
+    int state_store;   /* EXACT or F32 */
+    int sketch_store;  /* EXACT, F32 or BF16 */
+    int out_store;     /* EXACT, F32 or BF16 */
+} orc_layer;
+
+/* n independent tiles; every array is indexed by tile first. */
+typedef struct {
+    int n;
+    const int* rank;     /* [n] sketch rank of the tile's head */
+    double* S;           /* [n][dk][dv] stored state */
+    double* U;           /* [n][rmax][dv] stored sketch, row j = u_j = S^T p_j */
+    const double* Pt;    /* [n][rmax][dk] row j = column j of P_h (basis) */
+    const double* C;     /* [n][rmax][dk] row j = row j of C_h */
+    const double* A;     /* [n] Mamba-2 A_h (unused otherwise) */
+    double* rk;          /* [n][W][dk] ring keys */
+    double* rv;          /* [n][W][dv] ring values */
+    double* rg;          /* [n][W] (Mamba-2 dt, GDN alpha) or [n][W][dk] (KDA g) */
+    double* rb;          /* [n][W] GDN/KDA beta (unused for Mamba-2) */
+    int* count;          /* [n] entries buffered since the last flush */
+} orc_tiles;
+
+typedef struct {
+    const double* q;     /* [n][dk] */
+    const double* k;     /* [n][dk] */
+    const double* v;     /* [n][dv] */
+    const double* g;     /* [n] or [n][dk] (KDA) */
+    const double* b;     /* [n] (GDN/KDA) */
+    double* o;           /* [n][dv] */
+} orc_step;
+
+static int g_mutation = 0;
+void orc_set_mutation(int m) { g_mutation = m; }
+
+/* ------------------------------------------------------------ rounding */
+static double round_f32(double x) { return (double)(float)x; }
+
+static double round_bf16(double x) {
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double store(int mode, double x) {
+    if (mode == ORC_STORE_F32) return round_f32(x);
+    if (mode == ORC_STORE_BF16) return round_bf16(x);
+    return x;
+}
+
+static int gate_len(const orc_layer* L) { return L->family == ORC_KDA ? L->dk : 1; }
+
+static double dot(const double* x, const double* y, int n) {
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += x[i] * y[i];
+    return s;
+}
+
+/* Mamba-2 scalar decay a = exp(-dt * exp(A)). */
+static double m2_decay(double dt, double A) { return exp(-dt * exp(A)); }
+
+/* Write scale of B = s k v^T: dt for Mamba-2, beta for GDN/KDA. */
+static double write_scale(const orc_layer* L, const double* g, double beta) {
+    if (L->family == ORC_MAMBA2) return g_mutation == 8 ? 1.0 : g[0];
+    return beta;
+}
+
+/* S <- M S + s k v^T for one entry (k, v, gate g, beta), S is dk x dv. */
+static void apply_update(const orc_layer* L, double A, double* S,
+                         const double* k, const double* v, const double* g,
+                         double beta) {
+    const int dk = L->dk, dv = L->dv;
+    const double s = write_scale(L, g, beta);
+    if (L->family == ORC_MAMBA2) {
+        const double a = m2_decay(g[0], A);
+        for (int m = 0; m < dk; ++m)
+            for (int n = 0; n < dv; ++n) S[m * dv + n] = a * S[m * dv + n];
+    } else {
+        /* M S with M = alpha (I - beta k k^T) (GDN) or (I - beta k k^T) Diag(g) (KDA) */
+        const double esign = (g_mutation == 2) ? -1.0 : 1.0;
+        if (L->family == ORC_KDA && g_mutation != 6)
+            for (int m = 0; m < dk; ++m)
+                for (int n = 0; n < dv; ++n) S[m * dv + n] *= g[m];
+        double* kS = (double*)malloc(sizeof(double) * dv);   /* k^T S */
+        for (int n = 0; n < dv; ++n) {
+            double t = 0.0;
+            for (int m = 0; m < dk; ++m) t += k[m] * S[m * dv + n];
+            kS[n] = t;
+        }
+        for (int m = 0; m < dk; ++m)
+            for (int n = 0; n < dv; ++n)
+                S[m * dv + n] -= esign * beta * k[m] * kS[n];
+        free(kS);
+        if (L->family == ORC_KDA && g_mutation == 6)
+            for (int m = 0; m < dk; ++m)
+                for (int n = 0; n < dv; ++n) S[m * dv + n] *= g[m];
+        if (L->family == ORC_GDN)
+            for (int m = 0; m < dk; ++m)
+                for (int n = 0; n < dv; ++n) S[m * dv + n] *= g[0];
+    }
+    for (int m = 0; m < dk; ++m)
+        for (int n = 0; n < dv; ++n) S[m * dv + n] += s * k[m] * v[n];
+}
+
+/* r <- M^T r for one entry: Mamba-2 a r; GDN alpha (r - beta (k.r) k);
+ * KDA g (.) (r - beta (k.r) k). */
+static void pull_back(const orc_layer* L, double A, double* r, const double* k,
+                      const double* g, double beta) {
+    const int dk = L->dk;
+    if (g_mutation == 5) {
+        if (L->family == ORC_MAMBA2) return;
+    }
+    if (L->family == ORC_MAMBA2) {
+        const double a = m2_decay(g[0], A);
+        for (int m = 0; m < dk; ++m) r[m] *= a;
+        return;
+    }
+    const double d = dot(k, r, dk);
+    for (int m = 0; m < dk; ++m) r[m] -= beta * d * k[m];
+    if (g_mutation == 5) return;
+    if (L->family == ORC_GDN)
+        for (int m = 0; m < dk; ++m) r[m] *= g[0];
+    else
+        for (int m = 0; m < dk; ++m) r[m] *= g[m];
+}
+
+/* o = S^T x, S dk x dv. */
+static void state_read(const orc_layer* L, const double* S, const double* x, double* o) {
+    for (int n = 0; n < L->dv; ++n) {
+        double t = 0.0;
+        for (int m = 0; m < L->dk; ++m) t += S[m * L->dv + n] * x[m];
+        o[n] = t;
+    }
+}
+
+/* Tile accessors. */
+#define TS(T, L, i) ((T)->S + (size_t)(i) * (L)->dk * (L)->dv)
+#define TU(T, L, i) ((T)->U + (size_t)(i) * (L)->rmax * (L)->dv)
+#define TP(T, L, i) ((T)->Pt + (size_t)(i) * (L)->rmax * (L)->dk)
+#define TC(T, L, i) ((T)->C + (size_t)(i) * (L)->rmax * (L)->dk)
+#define RK(T, L, i, s) ((T)->rk + ((size_t)(i) * (L)->W + (s)) * (L)->dk)
+#define RV(T, L, i, s) ((T)->rv + ((size_t)(i) * (L)->W + (s)) * (L)->dv)
+#define RG(T, L, i, s) ((T)->rg + ((size_t)(i) * (L)->W + (s)) * gate_len(L))
+#define RB(T, L, i, s) ((T)->rb ? (T)->rb[(size_t)(i) * (L)->W + (s)] : 0.0)
+
+static double tile_A(const orc_tiles* T, int i) { return T->A ? T->A[i] : 0.0; }
+
+/* Append the step's (k, v, gate, beta) of tile i at ring slot count. */
+static void ring_append(const orc_layer* L, orc_tiles* T, const orc_step* st, int i) {
+    const int slot = T->count[i];
+    memcpy(RK(T, L, i, slot), st->k + (size_t)i * L->dk, sizeof(double) * L->dk);
+    memcpy(RV(T, L, i, slot), st->v + (size_t)i * L->dv, sizeof(double) * L->dv);
+    memcpy(RG(T, L, i, slot), st->g + (size_t)i * gate_len(L), sizeof(double) * gate_len(L));
+    if (T->rb) T->rb[(size_t)i * L->W + slot] = st->b ? st->b[i] : 0.0;
+    T->count[i] = slot + 1;
+}
+
+/* Pull the query back through ring entries n-1..0 (newest first): for each
+ * entry, d = k.r contributes s d v to the buffered output, then r <- M^T r.
+ * On return r = q~ (so that the state term is S0^T q~) and obuf holds the
+ * exact contribution of the buffered updates. */
+static void effective_query(const orc_layer* L, const orc_tiles* T, int i, int n,
+                            const double* q, double* r, double* obuf) {
+    const double A = tile_A(T, i);
+    memcpy(r, q, sizeof(double) * L->dk);
+    for (int j = 0; j < L->dv; ++j) obuf[j] = 0.0;
+    for (int t = 0; t < n; ++t) {
+        const int s = (g_mutation == 3) ? t : n - 1 - t;
+        const double* k = RK(T, L, i, s);
+        const double* g = RG(T, L, i, s);
+        const double beta = RB(T, L, i, s);
+        const double d = dot(k, r, L->dk);
+        const double w = write_scale(L, g, beta) * d;
+        const double* v = RV(T, L, i, s);
+        for (int j = 0; j < L->dv; ++j) obuf[j] += w * v[j];
+        pull_back(L, A, r, k, g, beta);
+    }
+}
+
+/* Apply ring entries 0..n-1 in order to the fp64 copy S of the stored state. */
+static void apply_ring(const orc_layer* L, const orc_tiles* T, int i, int n, double* S) {
+    const double A = tile_A(T, i);
+    for (int t = 0; t < n; ++t) {
+        const int s = (g_mutation == 7) ? n - 1 - t : t;
+        apply_update(L, A, S, RK(T, L, i, s), RV(T, L, i, s), RG(T, L, i, s), RB(T, L, i, s));
+    }
+}
+
+static void store_state(const orc_layer* L, orc_tiles* T, int i, const double* S) {
+    double* dst = TS(T, L, i);
+    for (int e = 0; e < L->dk * L->dv; ++e) dst[e] = store(L->state_store, S[e]);
+}
+
+/* u_j = S^T p_j for the tile's r_h basis vectors. */
+static void build_sketch(const orc_layer* L, orc_tiles* T, int i, const double* S) {
+    const int r = T->rank[i];
+    double* U = TU(T, L, i);
+    const double* P = TP(T, L, i);
+    double* u = (double*)malloc(sizeof(double) * L->dv);
+    for (int j = 0; j < r; ++j) {
+        state_read(L, S, P + (size_t)j * L->dk, u);
+        for (int n = 0; n < L->dv; ++n) U[(size_t)j * L->dv + n] = store(L->sketch_store, u[n]);
+    }
+    free(u);
+}
+
+static void write_out(const orc_layer* L, const orc_step* st, int i, const double* o) {
+    for (int n = 0; n < L->dv; ++n) st->o[(size_t)i * L->dv + n] = store(L->out_store, o[n]);
+}
+
+/* ------------------------------------------------------------------ API */
+
+/* Standard full-state step: S <- M S + B, o = S^T q, store S and o. */
+int orc_full_step(const orc_layer* L, orc_tiles* T, const orc_step* st) {
+    const size_t sz = (size_t)L->dk * L->dv;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < T->n; ++i) {
+        double* S = (double*)malloc(sizeof(double) * sz);
+        double* o = (double*)malloc(sizeof(double) * L->dv);
+        memcpy(S, TS(T, L, i), sizeof(double) * sz);
+        apply_update(L, tile_A(T, i), S, st->k + (size_t)i * L->dk, st->v + (size_t)i * L->dv,
+                     st->g + (size_t)i * gate_len(L), st->b ? st->b[i] : 0.0);
+        state_read(L, S, st->q + (size_t)i * L->dk, o);
+        store_state(L, T, i, S);
+        write_out(L, st, i, o);
+        free(S);
+        free(o);
+    }
+    return ORC_OK;
+}
+
+/* Flush: for every tile with count == W (or every tile, all != 0), apply the
+ * count buffered entries to the state in order, store the state, build the
+ * sketch from the updated state, write the exact output S^T q when a step is
+ * given, and empty the ring. */
+int orc_flush(const orc_layer* L, orc_tiles* T, const orc_step* st, int all) {
+    const size_t sz = (size_t)L->dk * L->dv;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int i = 0; i < T->n; ++i) {
+        const int n = T->count[i];
+        if (n < 0 || n > L->W) { err |= ORC_ERR_COUNT; continue; }
+        if (!all && n != L->W) continue;
+        double* S = (double*)malloc(sizeof(double) * sz);
+        double* o = (double*)malloc(sizeof(double) * L->dv);
+        double* S0 = (double*)malloc(sizeof(double) * sz);
+        memcpy(S, TS(T, L, i), sizeof(double) * sz);
+        memcpy(S0, S, sizeof(double) * sz);
+        apply_ring(L, T, i, n, S);
+        store_state(L, T, i, S);
+        build_sketch(L, T, i, S);
+        if (st && st->o) {
+            state_read(L, g_mutation == 10 ? S0 : S, st->q + (size_t)i * L->dk, o);
+            write_out(L, st, i, o);
+        }
+        T->count[i] = 0;
+        free(S);
+        free(S0);
+        free(o);
+    }
+    return err;
+}
+
+/* Sketched read (non-flush step): append the step's entry; if the window is
+ * not yet full, o = U (C q~) + o_buf from the stored sketch.  When the
+ * append fills the window (count == W) no output is written here: the flush
+ * produces it. */
+int orc_read(const orc_layer* L, orc_tiles* T, const orc_step* st) {
+    int err = ORC_OK;
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int i = 0; i < T->n; ++i) {
+        if (T->count[i] < 0 || T->count[i] >= L->W) { err |= ORC_ERR_COUNT; continue; }
+        ring_append(L, T, st, i);
+        const int n = T->count[i];
+        if (n == L->W) continue;
+        const int r = T->rank[i];
+        double* qt = (double*)malloc(sizeof(double) * L->dk);
+        double* obuf = (double*)malloc(sizeof(double) * L->dv);
+        double* c = (double*)malloc(sizeof(double) * (r > 0 ? r : 1));
+        double* o = (double*)malloc(sizeof(double) * L->dv);
+        const double* q = st->q + (size_t)i * L->dk;
+        effective_query(L, T, i, n, q, qt, obuf);
+        const double* C = TC(T, L, i);
+        const double* U = TU(T, L, i);
+        for (int j = 0; j < r; ++j)   /* c = C q~ */
+            c[j] = dot(C + (size_t)j * L->dk, g_mutation == 9 ? q : qt, L->dk);
+        for (int n2 = 0; n2 < L->dv; ++n2) {  /* o = U c + o_buf */
+            double t = (g_mutation == 1) ? 0.0 : obuf[n2];
+            for (int j = 0; j < r; ++j) {
+                const int jj = (g_mutation == 4) ? (j + 1) % r : j;
+                t += U[(size_t)jj * L->dv + n2] * c[j];
+            }
+            o[n2] = t;
+        }
+        write_out(L, st, i, o);
+        free(qt); free(obuf); free(c); free(o);
+    }
+    return err;
+}
+
+/* ReplaySSM step: append; before the window fills, o = S0^T q~ + o_buf read
+ * from the full stored state; when it fills, apply the W entries, store the
+ * state, o = S^T q from the updated state, and empty the ring. */
+int orc_replay_step(const orc_layer* L, orc_tiles* T, const orc_step* st) {
+    const size_t sz = (size_t)L->dk * L->dv;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int i = 0; i < T->n; ++i) {
+        if (T->count[i] < 0 || T->count[i] >= L->W) { err |= ORC_ERR_COUNT; continue; }
+        ring_append(L, T, st, i);
+        const int n = T->count[i];
+        double* o = (double*)malloc(sizeof(double) * L->dv);
+        const double* q = st->q + (size_t)i * L->dk;
+        if (n < L->W) {
+            double* qt = (double*)malloc(sizeof(double) * L->dk);
+            double* obuf = (double*)malloc(sizeof(double) * L->dv);
+            effective_query(L, T, i, n, q, qt, obuf);
+            state_read(L, TS(T, L, i), qt, o);
+            if (g_mutation != 1)
+                for (int j = 0; j < L->dv; ++j) o[j] += obuf[j];
+            free(qt); free(obuf);
+        } else {
+            double* S = (double*)malloc(sizeof(double) * sz);
+            memcpy(S, TS(T, L, i), sizeof(double) * sz);
+            apply_ring(L, T, i, n, S);
+            store_state(L, T, i, S);
+            state_read(L, S, q, o);
+            T->count[i] = 0;
+            free(S);
+        }
+        write_out(L, st, i, o);
+        free(o);
+    }
+    return err;
+}
+
+int orc_abi_version(void) { return 1; }
+
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+#else
+int orc_num_threads(void) { return 1; }
+void orc_set_num_threads(int n) { (void)n; }
+#endif
