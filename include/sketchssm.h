@@ -1,0 +1,165 @@
+/*
+ * sketchssm.h -- C ABI of the SketchSSM decode hot path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * SketchSSM ("Write to the Full State, Read from a Compact Sketch",
+ * arXiv 2609.33051) keeps the full recurrent state S of a linear-attention /
+ * SSM head exact but reads it only once per window of W decode steps:
+ *
+ *   - flush (every W steps): read S once, apply the W buffered updates from
+ *     the ring, build the sketch U = S^T P from the updated state with a fixed
+ *     per-head basis P, write back S and U (project page, "02 / How to make a
+ *     sketch", per-window flush panel; paper App. B);
+ *   - read (the other W-1 steps): o = U (C q~) plus the exact contribution of
+ *     the buffered updates, where q~ is the query pulled back through the
+ *     buffered transitions; S is not read (project page, per-step non-flush
+ *     panel; paper Sec. 3.2 and App. C.1).
+ *
+ * Two baselines share the layout: the standard full-state step (read and
+ * write S every step; project page "01 / The idea", S_t = M_t S_{t-1} + B_t,
+ * o_t = S_t^T q_t) and ReplaySSM (buffered writes, full-state read every
+ * step; paper Sec. 1-2 and App. D).
+ *
+ * Families (per (sequence, head) tile; S is dk x dv, o = S^T q):
+ *   SKSSM_MAMBA2: S <- a S + dt k v^T,  a = exp(-dt * exp(A_h)); q~ = (prod a) q
+ *   SKSSM_GDN:    S <- alpha (I - beta k k^T) S + beta k v^T
+ *   SKSSM_KDA:    S <- (I - beta k k^T) Diag(g) S + beta k v^T
+ *
+ * Memory and ownership
+ *   - Every pointer inside sketchssm_buffers / sketchssm_step is a DEVICE
+ *     pointer owned by the caller.  sketchssm_layer and its rank_offsets_host
+ *     table are HOST memory, read during the call only and never retained.
+ *   - The library allocates nothing, keeps no state between calls and never
+ *     synchronises: every call only enqueues kernels on the caller's HIP
+ *     stream (NULL = the default stream).  Buffers must not be reused until
+ *     stream order guarantees completion.  Calls on different layers may run
+ *     concurrently on different streams; calls on one layer must be ordered.
+ *   - Calls are re-entrant; no C++ exception crosses the ABI.
+ *
+ * Errors
+ *   - The return value is 0 on success or a negative SKSSM_E* code.
+ *     Arguments are validated on the host, synchronously; on failure nothing
+ *     is launched and nothing is written.
+ *   - SKSSM_ELAUNCH reports a failed launch (hipGetLastError after it).
+ *   - Semantic faults found by the kernels (a ring count outside [0, W], a
+ *     read of a sequence whose window is already full, inconsistent counts
+ *     within a Mamba-2 B/C group) leave that tile untouched and OR a
+ *     SKSSM_ERRBIT_* bit into *err; the caller reads it after synchronising.
+ *   - Device faults surface at the caller's next synchronisation.
+ */
+#ifndef SKETCHSSM_H
+#define SKETCHSSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* families */
+#define SKSSM_MAMBA2 0
+#define SKSSM_GDN 1
+#define SKSSM_KDA 2
+
+/* dtypes */
+#define SKSSM_F32 0
+#define SKSSM_BF16 1
+
+/* flush flags */
+#define SKSSM_FLUSH_DUE 0 /* flush tiles whose ring holds W entries */
+#define SKSSM_FLUSH_ALL 1 /* flush every tile (prime U, or retire sequences) */
+
+/* return codes */
+#define SKSSM_OK 0
+#define SKSSM_EINVAL -1  /* NULL or misaligned pointer (16-byte alignment) */
+#define SKSSM_EDIM -2    /* unsupported shape, W, ranks or rank table */
+#define SKSSM_EDTYPE -3  /* unsupported dtype combination */
+#define SKSSM_EFLAG -4   /* unknown flag */
+#define SKSSM_ELAUNCH -5 /* kernel launch failed */
+
+/* bits OR-ed into *err by the kernels */
+#define SKSSM_ERRBIT_COUNT 1  /* count outside [0, W] (or == W at a read) */
+#define SKSSM_ERRBIT_GROUP 2  /* Mamba-2 heads of one B/C group disagree on count */
+
+/* Supported shapes: (dk, dv) in {(16,32), (64,64), (128,64), (128,128)};
+ * 1 <= W <= 32; 1 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16;
+ * heads % qk_groups == 0 (qk_groups == heads for GDN/KDA). */
+typedef struct {
+  int32_t family;            /* SKSSM_MAMBA2 | SKSSM_GDN | SKSSM_KDA */
+  int32_t batch;             /* B sequences */
+  int32_t heads;             /* H state heads */
+  int32_t qk_groups;         /* G: Mamba-2 B/C groups (heads h in group h / (H/G)); GDN/KDA: = H */
+  int32_t dk, dv;            /* state is dk x dv per (sequence, head) */
+  int32_t window;            /* W: one flush every W steps */
+  int32_t act_dtype;         /* dtype of q, k, v, o, Mamba-2 dt and the ring's k, v, dt */
+  int32_t sketch_dtype;      /* dtype of U */
+  const int32_t* rank_offsets_host; /* [H+1] host copy: exclusive prefix sum of r_h */
+} sketchssm_layer;
+
+typedef struct {
+  float* S;                  /* [B][H][dk][dv] fp32, dv fastest */
+  void* U;                   /* [B][R][dv] sketch dtype, R = offsets[H]; rows
+                                off_h..off_h+r_h-1 hold u_j = S^T p_j of head h */
+  const float* Pt;           /* [R][dk] fp32: row off_h + j = column j of P_h */
+  const float* C;            /* [R][dk] fp32: row off_h + j = row j of C_h (r_h x dk) */
+  const int32_t* rank_offsets; /* [H+1] device copy of rank_offsets_host */
+  void* ring_k;              /* [B][G][W][dk] act dtype */
+  void* ring_v;              /* [B][H][W][dv] act dtype */
+  void* ring_gate;           /* Mamba-2: dt [B][H][W] act dtype; GDN: alpha [B][H][W] fp32;
+                                KDA: g [B][H][W][dk] fp32 */
+  float* ring_beta;          /* GDN/KDA: [B][H][W] fp32; NULL for Mamba-2 */
+  int32_t* count;            /* [B][H]: entries buffered in tile (b,h) since its last flush,
+                                0..W; every head of a sequence advances together */
+  const float* A;            /* Mamba-2: [H] fp32; NULL otherwise */
+  int32_t* err;              /* [1] device error word (SKSSM_ERRBIT_*), never cleared here */
+} sketchssm_buffers;
+
+typedef struct {             /* one decode step */
+  const void* q;             /* [B][G][dk] act dtype */
+  const void* k;             /* [B][G][dk] act dtype */
+  const void* v;             /* [B][H][dv] act dtype */
+  const void* gate;          /* Mamba-2: dt [B][H] act dtype; GDN: alpha [B][H] fp32;
+                                KDA: g [B][H][dk] fp32 */
+  const float* beta;         /* GDN/KDA: [B][H] fp32; NULL for Mamba-2 */
+  void* o;                   /* [B][H][dv] act dtype (output) */
+} sketchssm_step;
+
+/* Non-flush sketched read (project page, per-step non-flush panel: c = C q~,
+ * o^ = U c, plus the exact buffered contribution; paper Sec. 3.2 and
+ * App. C.1 for q~).  For every tile: append the step's (k, v, gate, beta) at
+ * ring slot count, count += 1; if count < W write o = U (C q~) + o_buf,
+ * otherwise leave o for sketchssm_flush.  Never reads S. */
+int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                   const sketchssm_step* step, void* hip_stream);
+
+/* Flush (paper App. B; project page per-window flush panel: U = S^T Omega,
+ * fused into the update).  For every tile with count == W (flags =
+ * SKSSM_FLUSH_DUE) or every tile (SKSSM_FLUSH_ALL): apply the count buffered
+ * entries to S in order, write S, write U = S^T P from the updated state,
+ * set count = 0 and, if step != NULL, write the exact output o = S^T q.
+ * FLUSH_ALL with count == 0 primes U from the current state. */
+int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                    const sketchssm_step* step /* NULL: no output */, int32_t flags,
+                    void* hip_stream);
+
+/* Standard full-state step (project page "01 / The idea": S_t = M_t S_{t-1}
+ * + B_t, o_t = S_t^T q_t): S <- M S + B and o = S^T q for every tile.
+ * Ignores the ring, count, U, Pt and C. */
+int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                        const sketchssm_step* step, void* hip_stream);
+
+/* ReplaySSM step (paper Sec. 1-2 and App. D: buffer writes for W steps,
+ * read the full state every step).  Append as sketchssm_read; if count < W
+ * write the exact o = S0^T q~ + o_buf reading S in full; if count == W apply
+ * the W entries, write S, o = S^T q, count = 0.  Does not touch U. */
+int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                          const sketchssm_step* step, void* hip_stream);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int sketchssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKETCHSSM_H */

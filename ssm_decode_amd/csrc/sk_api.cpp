@@ -1,0 +1,191 @@
+// C ABI of the SketchSSM decode library: host-side validation and dispatch.
+// Every check runs before any HIP call, so an invalid call launches nothing
+// and writes nothing.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/sketchssm.h"
+#include "sk_params.hpp"
+
+namespace {
+
+constexpr int kMaxW = 32;
+constexpr int kMaxRank = 16;
+constexpr int kMaxHeadsPerGroup = 16;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_supported(int dk, int dv) {
+  return (dk == 16 && dv == 32) || (dk == 64 && dv == 64) || (dk == 128 && dv == 64) ||
+         (dk == 128 && dv == 128);
+}
+
+// What a call needs from the buffers and the step.
+struct Needs {
+  bool S, U, Pt, C, ring, count, step_in, step_q, step_o;
+};
+
+int check_layer(const sketchssm_layer* L) {
+  if (!L) return SKSSM_EINVAL;
+  if (L->family < SKSSM_MAMBA2 || L->family > SKSSM_KDA) return SKSSM_EDIM;
+  if (L->act_dtype < SKSSM_F32 || L->act_dtype > SKSSM_BF16) return SKSSM_EDTYPE;
+  if (L->sketch_dtype < SKSSM_F32 || L->sketch_dtype > SKSSM_BF16) return SKSSM_EDTYPE;
+  if (L->act_dtype != L->sketch_dtype) return SKSSM_EDTYPE;   // (f32, f32) or (bf16, bf16)
+  if (L->batch < 0 || L->heads < 1 || L->qk_groups < 1) return SKSSM_EDIM;
+  if (L->heads % L->qk_groups != 0) return SKSSM_EDIM;
+  if (L->family == SKSSM_MAMBA2) {
+    if (L->heads / L->qk_groups > kMaxHeadsPerGroup) return SKSSM_EDIM;
+  } else if (L->qk_groups != L->heads) {
+    return SKSSM_EDIM;
+  }
+  if (!shape_supported(L->dk, L->dv)) return SKSSM_EDIM;
+  if (L->window < 1 || L->window > kMaxW) return SKSSM_EDIM;
+  if ((int64_t)L->batch * L->heads > INT32_MAX / 2) return SKSSM_EDIM;
+  if (!L->rank_offsets_host) return SKSSM_EINVAL;
+  const int32_t* off = L->rank_offsets_host;
+  if (off[0] != 0) return SKSSM_EDIM;
+  const int rmax = L->dk < kMaxRank ? L->dk : kMaxRank;
+  for (int h = 0; h < L->heads; ++h) {
+    const int r = off[h + 1] - off[h];
+    if (r < 1 || r > rmax) return SKSSM_EDIM;
+  }
+  return SKSSM_OK;
+}
+
+int check_buffers(const sketchssm_layer* L, const sketchssm_buffers* B, const sketchssm_step* S,
+                  const Needs& nd) {
+  if (!B) return SKSSM_EINVAL;
+  if (nd.S && !aligned16(B->S)) return SKSSM_EINVAL;
+  if (nd.U && !aligned16(B->U)) return SKSSM_EINVAL;
+  if (nd.Pt && !aligned16(B->Pt)) return SKSSM_EINVAL;
+  if (nd.C && !aligned16(B->C)) return SKSSM_EINVAL;
+  if ((nd.U || nd.Pt || nd.C) && !aligned16(B->rank_offsets)) return SKSSM_EINVAL;
+  if (nd.ring) {
+    if (!aligned16(B->ring_k) || !aligned16(B->ring_v) || !aligned16(B->ring_gate)) return SKSSM_EINVAL;
+    if (L->family != SKSSM_MAMBA2 && !aligned16(B->ring_beta)) return SKSSM_EINVAL;
+  }
+  if (nd.count && (!aligned16(B->count) || !aligned16(B->err))) return SKSSM_EINVAL;
+  if (L->family == SKSSM_MAMBA2 && !aligned16(B->A)) return SKSSM_EINVAL;
+  if (nd.step_in || nd.step_q || nd.step_o) {
+    if (!S) return SKSSM_EINVAL;
+    if (nd.step_in) {
+      if (!aligned16(S->k) || !aligned16(S->v) || !aligned16(S->gate)) return SKSSM_EINVAL;
+      if (L->family != SKSSM_MAMBA2 && !aligned16(S->beta)) return SKSSM_EINVAL;
+    }
+    if (nd.step_q && !aligned16(S->q)) return SKSSM_EINVAL;
+    if (nd.step_o && !aligned16(S->o)) return SKSSM_EINVAL;
+  }
+  return SKSSM_OK;
+}
+
+sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, const sketchssm_step* S) {
+  sk::Params p{};
+  p.B = L->batch;
+  p.H = L->heads;
+  p.G = L->qk_groups;
+  p.HPG = L->heads / L->qk_groups;
+  p.W = L->window;
+  p.R = L->rank_offsets_host[L->heads];
+  p.S = B->S;
+  p.U = B->U;
+  p.Pt = B->Pt;
+  p.C = B->C;
+  p.off = B->rank_offsets;
+  p.rk = B->ring_k;
+  p.rv = B->ring_v;
+  p.rg = B->ring_gate;
+  p.rb = B->ring_beta;
+  p.count = B->count;
+  p.A = B->A;
+  p.err = B->err;
+  if (S) {
+    p.q = S->q;
+    p.k = S->k;
+    p.v = S->v;
+    p.gate = S->gate;
+    p.beta = S->beta;
+    p.o = S->o;
+  }
+  return p;
+}
+
+int dispatch(const sketchssm_layer* L, int mode, const sk::Params& p, void* stream) {
+  if (L->batch == 0) return SKSSM_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int rc;
+  switch (L->family) {
+    case SKSSM_MAMBA2: rc = sk::launch_m2(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+    case SKSSM_GDN: rc = sk::launch_gdn(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+    default: rc = sk::launch_kda(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+  }
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                   const sketchssm_step* step, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    const Needs nd{false, true, false, true, true, true, true, true, true};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    return dispatch(layer, sk::MODE_READ, make_params(layer, bufs, step), hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                    const sketchssm_step* step, int32_t flags, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL) return SKSSM_EFLAG;
+    const bool out = step != nullptr;
+    const Needs nd{true, true, true, false, true, true, false, out, out};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    sk::Params p = make_params(layer, bufs, step);
+    p.flush_all = flags == SKSSM_FLUSH_ALL;
+    if (!out) {
+      p.q = nullptr;
+      p.o = nullptr;
+    }
+    return dispatch(layer, sk::MODE_FLUSH, p, hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                        const sketchssm_step* step, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    const Needs nd{true, false, false, false, false, false, true, true, true};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    return dispatch(layer, sk::MODE_FULL, make_params(layer, bufs, step), hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                          const sketchssm_step* step, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    const Needs nd{true, false, false, false, true, true, true, true, true};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    return dispatch(layer, sk::MODE_REPLAY, make_params(layer, bufs, step), hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int sketchssm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers for the SketchSSM decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+typedef uint16_t bf16;  // storage type of bfloat16 values
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float((uint32_t)x << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ float cvt(float x) { return x; }
+};
+template <> struct Store<bf16> {
+  static __device__ __forceinline__ bf16 cvt(float x) { return f32_to_bf16(x); }
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
+
+// Four consecutive elements as fp32.
+__device__ __forceinline__ void ld4(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void ld4(const bf16* p, float (&x)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(v.x << 16);
+  x[1] = __uint_as_float(v.x & 0xffff0000u);
+  x[2] = __uint_as_float(v.y << 16);
+  x[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void st4(float* p, const float (&x)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void st4(bf16* p, const float (&x)[4]) {
+  uint2 v;
+  v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, float x) { *p = Store<T>::cvt(x); }
+
+// Sum of x over the lanes that differ in lane bits [LB, LB+NB); every lane
+// receives the total.
+template <int LB, int NB>
+__device__ __forceinline__ float xsum(float x) {
+#pragma unroll
+  for (int s = 0; s < NB; ++s) x += __shfl_xor(x, 1 << (LB + s));
+  return x;
+}
+
+// Reduce a[0..N) across the 2^NB lanes that differ in lane bits
+// [LB, LB+NB), halving the vector at every exchange.  Afterwards a lane holds
+// in a[0..N>>NB) the sums of elements [sel*(N>>NB), (sel+1)*(N>>NB)) where
+// sel = (lane >> LB) & (2^NB - 1).  Requires N >= 2^NB.
+template <int N, int LB, int NB>
+__device__ __forceinline__ void tr_reduce(float (&a)[N], int lane) {
+  static_assert(N >= (1 << NB), "tr_reduce: vector shorter than the lane group");
+#pragma unroll
+  for (int s = NB - 1; s >= 0; --s) {
+    const int mask = 1 << (LB + s);
+    const bool up = (lane & mask) != 0;
+    const int half = (N >> (NB - 1 - s)) / 2;
+#pragma unroll
+    for (int e = 0; e < half; ++e) {
+      const float send = up ? a[e] : a[e + half];
+      const float keep = up ? a[e + half] : a[e];
+      a[e] = keep + __shfl_xor(send, mask);
+    }
+  }
+}
+
+// Mamba-2 decay a = exp(-dt * exp(A)).
+__device__ __forceinline__ float m2_decay(float dt, float A) { return __expf(-dt * __expf(A)); }
+
+}  // namespace sk

@@ -1,0 +1,49 @@
+// Per-family launch dispatch over the supported shapes and dtypes.  Each
+// family's translation unit includes this file once with its own FAMILY.
+#pragma once
+
+#include "sk_read.hpp"
+#include "sk_tile.hpp"
+
+namespace sk {
+
+template <int FAM, int DK, int DV, typename AT, typename UT>
+static int launch_shape(int mode, const Params& p, hipStream_t st) {
+  if (p.B <= 0 || p.H <= 0) return 0;
+  if (mode == MODE_READ) {
+    if (FAM == FAM_M2)
+      hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT>), dim3(p.B * p.G), dim3(M2R_THREADS), 0, st, p);
+    else
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT>), dim3(p.B * p.H), dim3(64), 0, st, p);
+  } else {
+    const size_t lds = sizeof(float) * tile_lds_floats<FAM, DK, DV>(p.W);
+    const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
+    if (mode == MODE_FLUSH)
+      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH>), grid, block, lds, st, p);
+    else if (mode == MODE_FULL)
+      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL>), grid, block, lds, st, p);
+    else if (mode == MODE_REPLAY)
+      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY>), grid, block, lds, st, p);
+    else
+      return -4;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <int FAM, typename AT, typename UT>
+static int launch_dtype(int mode, int dk, int dv, const Params& p, hipStream_t st) {
+  if (dk == 16 && dv == 32) return launch_shape<FAM, 16, 32, AT, UT>(mode, p, st);
+  if (dk == 64 && dv == 64) return launch_shape<FAM, 64, 64, AT, UT>(mode, p, st);
+  if (dk == 128 && dv == 64) return launch_shape<FAM, 128, 64, AT, UT>(mode, p, st);
+  if (dk == 128 && dv == 128) return launch_shape<FAM, 128, 128, AT, UT>(mode, p, st);
+  return -2;
+}
+
+template <int FAM>
+static int launch_family(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
+  if (act == DT_F32 && sketch == DT_F32) return launch_dtype<FAM, float, float>(mode, dk, dv, p, st);
+  if (act == DT_BF16 && sketch == DT_BF16) return launch_dtype<FAM, bf16, bf16>(mode, dk, dv, p, st);
+  return -3;
+}
+
+}  // namespace sk

@@ -1,0 +1,43 @@
+// Kernel argument block shared by the launchers and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+enum Family { FAM_M2 = 0, FAM_GDN = 1, FAM_KDA = 2 };
+enum Mode { MODE_FLUSH = 0, MODE_FULL = 1, MODE_REPLAY = 2, MODE_READ = 3 };
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+enum ErrBit { ERRBIT_COUNT = 1, ERRBIT_GROUP = 2 };
+
+struct Params {
+  int B, H, G, HPG, W, R;
+  int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
+  float* S;
+  void* U;
+  const float* Pt;
+  const float* C;
+  const int32_t* off;   // [H+1] device rank offsets
+  void* rk;
+  void* rv;
+  void* rg;
+  float* rb;
+  int32_t* count;
+  const float* A;
+  int32_t* err;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;
+  const float* beta;
+  void* o;
+};
+
+// Launch one kernel of `family` for `mode`; returns 0, or -2 when the shape
+// / dtype combination has no instantiation, or -5 on a launch error.
+int launch_m2(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+int launch_gdn(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+int launch_kda(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+
+}  // namespace sk

@@ -1,0 +1,168 @@
+"""Drives the HIP path (through the C ABI) and the oracle side by side on the
+same seeded inputs and compares them step by step (test infrastructure)."""
+from __future__ import annotations
+
+import sys
+import time
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from ssm_decode_amd import abi, feed
+
+TOL_F32 = 1e-5
+TOL_BF16 = 1e-2
+
+
+def rel_l2(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / den) if den > 0 else float(np.linalg.norm(x))
+
+
+def tol_out(cfg) -> float:
+    return TOL_F32 if cfg.act == "f32" else TOL_BF16
+
+
+def tol_sketch(cfg) -> float:
+    return TOL_F32 if cfg.sketch == "f32" else TOL_BF16
+
+
+@dataclass
+class ParityReport:
+    name: str
+    method: str
+    steps: int
+    tiles: int
+    max_o: float = 0.0
+    max_S: float = 0.0
+    max_U: float = 0.0
+    flushes: int = 0
+    count_mismatch: int = 0
+    err_word: int = 0
+    seconds: float = 0.0
+    per_step_o: list = field(default_factory=list)
+
+    def line(self) -> str:
+        return (f"{self.name} {self.method}: steps={self.steps} tiles={self.tiles} "
+                f"max rel-L2 o={self.max_o:.3e} S={self.max_S:.3e} U={self.max_U:.3e} "
+                f"flush-steps={self.flushes} count-mismatch={self.count_mismatch} "
+                f"err={self.err_word} ({self.seconds:.1f}s)")
+
+
+def sample_tiles(cfg, n_seq: int, n_head: int, seed: int = 0) -> np.ndarray:
+    """Sequences spread over the batch (first, last, random) x heads spread
+    over the head range (first, last, random)."""
+    rng = np.random.default_rng(1000 + seed)
+    bs = {0, cfg.batch - 1} | set(rng.choice(cfg.batch, size=min(cfg.batch, n_seq), replace=False).tolist())
+    hs = {0, cfg.heads - 1} | set(rng.choice(cfg.heads, size=min(cfg.heads, n_head), replace=False).tolist())
+    return np.array([(b, h) for b in sorted(bs) for h in sorted(hs)], dtype=np.int64)
+
+
+def all_tiles(cfg) -> np.ndarray:
+    return np.array([(b, h) for b in range(cfg.batch) for h in range(cfg.heads)], dtype=np.int64)
+
+
+def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray = None,
+               numpy_all: bool = True, li: synth.LayerInputs = None, log=True) -> ParityReport:
+    t0 = time.time()
+    steps = cfg.steps if steps is None else steps
+    li = synth.make_layer_inputs(cfg) if li is None else li
+    tiles = all_tiles(cfg) if tiles is None else tiles
+    seqs = np.unique(tiles[:, 0])
+    seq_rows = np.full(cfg.batch, -1, dtype=np.int64)
+    seq_rows[seqs] = np.arange(len(seqs))
+    W = cfg.window
+
+    # --- HIP side
+    lay = feed.make_layer(cfg, li)
+    feed.fill_state(lay, cfg, exact_seqs=seqs, numpy_all=numpy_all)
+    # --- oracle side
+    S0s = synth.initial_state(cfg, b_idx=seqs)
+    S0_t = S0s[seq_rows[tiles[:, 0]], tiles[:, 1]]
+    orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, W, li.ranks, li.offsets, li.Pt, li.C, li.A,
+                             tiles, S0_t, cfg.heads, cfg.qk_groups, state_store="f32",
+                             sketch_store=cfg.sketch, out_store=cfg.act)
+    count0_t = li.count0[tiles[:, 0], tiles[:, 1]]
+    if method == "sketch":
+        assert feed.prime(lay, li) == 0
+        rc, _ = orc.flush(None, all_tiles=True)
+        assert rc == 0
+    else:
+        lay.count.copy_(torch.from_numpy(li.count0).to(lay.device))
+    orc.count[:] = count0_t if method != "standard" else 0
+
+    rep = ParityReport(cfg.name, method, steps, len(tiles))
+    step = lay.new_step()
+    tb = torch.from_numpy(tiles[:, 0]).to(lay.device)
+    th = torch.from_numpy(tiles[:, 1]).to(lay.device)
+    t_o, t_s = tol_out(cfg), tol_sketch(cfg)
+    for t in range(steps):
+        feed.fill_step(step, cfg, t, exact_seqs=seqs, numpy_all=numpy_all)
+        si = synth.make_step_inputs(cfg, t, b_idx=seqs)
+        o_ref = np.zeros((len(tiles), cfg.dv))
+        if method == "sketch":
+            assert lay.read(step) == 0
+            assert lay.flush(step, abi.SKSSM_FLUSH_DUE) == 0
+            rc, _ = orc.read(si, seq_rows=seq_rows, o=o_ref)
+            assert rc == 0
+            due = orc.count == W
+            if due.any():
+                rc, _ = orc.flush(si, seq_rows=seq_rows, o=o_ref)
+                assert rc == 0
+        elif method == "replay":
+            assert lay.replay_step(step) == 0
+            rc, _ = orc.replay_step(si, seq_rows=seq_rows, o=o_ref)
+            assert rc == 0
+            due = orc.count == 0
+        elif method == "standard":
+            assert lay.full_step(step) == 0
+            rc, _ = orc.full_step(si, seq_rows=seq_rows, o=o_ref)
+            assert rc == 0
+            due = np.ones(len(tiles), dtype=bool)
+        else:
+            raise ValueError(method)
+        torch.cuda.synchronize()
+        o_gpu = step.o[tb, th].float().cpu().numpy().astype(np.float64)
+        e = rel_l2(o_gpu, o_ref)
+        rep.per_step_o.append(e)
+        rep.max_o = max(rep.max_o, e)
+        if method != "standard":
+            cnt = lay.count.cpu().numpy()
+            want = (t - li.phase[:, None]) % W
+            rep.count_mismatch += int((cnt != np.broadcast_to(want, cnt.shape)).sum())
+            rep.count_mismatch += int((cnt[tiles[:, 0], tiles[:, 1]] != orc.count).sum())
+        if due.any():
+            rep.flushes += 1
+            sel = np.nonzero(due)[0]
+            sb = torch.from_numpy(tiles[sel, 0]).to(lay.device)
+            sh = torch.from_numpy(tiles[sel, 1]).to(lay.device)
+            S_gpu = lay.S[sb, sh].cpu().numpy().astype(np.float64)
+            rep.max_S = max(rep.max_S, rel_l2(S_gpu, orc.S[sel]))
+            if method == "sketch":
+                U_gpu = lay.U[tiles[sel, 0]].float().cpu().numpy().astype(np.float64)
+                Ug, Uo = [], []
+                for i, ti in enumerate(sel):
+                    h = tiles[ti, 1]
+                    off, r = li.offsets[h], li.ranks[h]
+                    Ug.append(U_gpu[i, off:off + r])
+                    Uo.append(orc.U[ti, :r])
+                rep.max_U = max(rep.max_U, rel_l2(np.concatenate(Ug), np.concatenate(Uo)))
+        if log and (t % 16 == 15 or t == steps - 1):
+            print(f"  [{cfg.name} {method}] step {t + 1}/{steps} max o={rep.max_o:.2e} "
+                  f"S={rep.max_S:.2e} U={rep.max_U:.2e}", flush=True)
+        assert e <= t_o, f"{cfg.name} {method} step {t}: rel-L2(o) = {e:.3e} > {t_o}"
+    rep.err_word = lay.error_word()
+    rep.seconds = time.time() - t0
+    assert rep.count_mismatch == 0, rep.line()
+    assert rep.max_S <= TOL_F32, rep.line()
+    assert rep.max_U <= t_s, rep.line()
+    assert rep.err_word == 0, rep.line()
+    if log:
+        print("  " + rep.line(), flush=True)
+        sys.stdout.flush()
+    return rep

@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every entry point its header declares,
+and rejects invalid arguments on the host without launching anything (runs
+without a GPU: every call here fails validation or has batch 0)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from ssm_decode_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sketchssm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(abi.LIB_PATH):
+        from ssm_decode_amd.build import build
+        build()
+    return abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^int\s+(sketchssm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(abi.ENTRY_POINTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert abi.sketchssm_version() == 100
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SKSSM_\w+)\s+(-?\d+)", text))
+    for k, v in consts.items():
+        assert getattr(abi, k) == v, k
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def _layer(offsets, family=abi.SKSSM_MAMBA2, batch=2, heads=4, groups=4, dk=16, dv=32, W=4,
+           act=abi.SKSSM_F32, sk=abi.SKSSM_F32):
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    L = abi.sketchssm_layer(family, batch, heads, groups, dk, dv, W, act, sk,
+                            off.ctypes.data_as(C.POINTER(C.c_int32)))
+    L._keep = off
+    return L
+
+
+def _bufs(**over):
+    f = dict(S=FAKE, U=FAKE, Pt=FAKE, C=FAKE, rank_offsets=FAKE, ring_k=FAKE, ring_v=FAKE,
+             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE)
+    f.update(over)
+    return abi.sketchssm_buffers(**f)
+
+
+def _step(**over):
+    f = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, o=FAKE)
+    f.update(over)
+    return abi.sketchssm_step(**f)
+
+
+OK_OFF = [0, 4, 8, 12, 16]
+
+
+def _all_calls(L, B, S, flags=abi.SKSSM_FLUSH_DUE):
+    return [abi.sketchssm_read(L, B, S), abi.sketchssm_flush(L, B, S, flags),
+            abi.sketchssm_full_step(L, B, S), abi.sketchssm_replay_step(L, B, S)]
+
+
+def test_batch_zero_is_a_no_op(lib):
+    assert _all_calls(_layer(OK_OFF, batch=0), _bufs(), _step()) == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(family=3), abi.SKSSM_EDIM),
+    (dict(act=abi.SKSSM_BF16), abi.SKSSM_EDTYPE),          # act != sketch dtype
+    (dict(act=2, sk=2), abi.SKSSM_EDTYPE),
+    (dict(dk=32, dv=32), abi.SKSSM_EDIM),
+    (dict(W=0), abi.SKSSM_EDIM),
+    (dict(W=33), abi.SKSSM_EDIM),
+    (dict(heads=4, groups=3), abi.SKSSM_EDIM),
+    (dict(family=abi.SKSSM_GDN, groups=2), abi.SKSSM_EDIM),
+    (dict(batch=-1), abi.SKSSM_EDIM),
+])
+def test_bad_layer(lib, kw, code):
+    assert _all_calls(_layer(OK_OFF, **kw), _bufs(), _step()) == [code] * 4
+
+
+def test_heads_per_group_limit(lib):
+    off = list(range(0, 4 * 33, 4))
+    L = _layer(off, heads=32, groups=1)
+    L2 = _layer(off, heads=32, groups=2)
+    assert abi.sketchssm_read(L, _bufs(), _step()) == abi.SKSSM_EDIM
+    assert abi.sketchssm_read(_layer(off, heads=32, groups=2, batch=0), _bufs(), _step()) == 0
+    del L2
+
+
+@pytest.mark.parametrize("off", [[1, 4, 8, 12, 16], [0, 0, 4, 8, 12], [0, 4, 8, 12, 29],
+                                 [0, 4, 3, 8, 12]])
+def test_bad_rank_table(lib, off):
+    assert _all_calls(_layer(off), _bufs(), _step()) == [abi.SKSSM_EDIM] * 4
+
+
+def test_rank_limit_is_min_dk_16(lib):
+    L = _layer([0, 16, 32, 48, 64], batch=0)          # r = dk = 16 allowed
+    assert _all_calls(L, _bufs(), _step()) == [0] * 4
+    L = _layer([0, 17, 34, 51, 68], dk=128, dv=64, batch=1)
+    assert _all_calls(L, _bufs(), _step()) == [abi.SKSSM_EDIM] * 4
+
+
+def test_null_and_misaligned_pointers(lib):
+    L = _layer(OK_OFF)
+    assert abi.sketchssm_read(None, _bufs(), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, None, _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(), None) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_full_step(L, _bufs(), None) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_replay_step(L, _bufs(), None) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_flush(L, _bufs(S=FAKE + 4), None, abi.SKSSM_FLUSH_ALL) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_flush(L, _bufs(U=None), None, abi.SKSSM_FLUSH_ALL) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(C=FAKE + 8), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(), _step(o=FAKE + 2)) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(A=None), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_replay_step(L, _bufs(count=None), _step()) == abi.SKSSM_EINVAL
+    Lg = _layer(OK_OFF, family=abi.SKSSM_GDN)
+    assert abi.sketchssm_read(Lg, _bufs(ring_beta=None), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(Lg, _bufs(), _step(beta=None)) == abi.SKSSM_EINVAL
+    # a flush without a step writes no output and needs no step pointers
+    assert abi.sketchssm_flush(_layer(OK_OFF, batch=0), _bufs(), None, abi.SKSSM_FLUSH_ALL) == 0
+
+
+def test_bad_flag(lib):
+    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 2) == abi.SKSSM_EFLAG
+    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, -1) == abi.SKSSM_EFLAG
