@@ -1,0 +1,349 @@
+"""Benchmark of the SketchSSM decode hot path on one MI355X.
+
+One step = one decode step of one layer: the non-flush sketched read, plus
+the flush on the step that closes a window.  The workload is the Mamba-2
+layer at batch 320 (128 heads, dk 128, dv 64, 8 B/C groups, W = 16, mean
+sketch rank 8, bf16 activations and sketch, fp32 state).  L independent
+instances of the layer are rotated every step (as consecutive layers of a
+model would be), so that the non-flush working set of one instance does not
+stay in the 256 MiB last-level cache between its steps.
+
+Printed: one JSON line with the per-layer step time (W-amortised, µs), the
+achieved HBM bandwidth of the algorithmic bytes, the roofline of the
+dominant kernel (the flush) timed with HIP events on its stream, GPU
+baselines (standard full-state step, ReplaySSM step), and the CPU oracle
+timed on a bounded sample as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=160, help="timed decode steps (per layer)")
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="m2_b320")
+    ap.add_argument("--layers", type=int, default=0, help="rotated layer instances (0: auto)")
+    ap.add_argument("--pool", type=int, default=16, help="device-resident step inputs cycled")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-baselines", action="store_true", help="skip full/replay GPU baselines")
+    ap.add_argument("--cpu-seqs", type=int, default=160, help="sequences in the CPU sample")
+    ap.add_argument("--cpu-windows", type=int, default=2, help="windows in the CPU sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this decode path has no multi-GPU mode "
+              "(its (sequence, head) tiles are independent; sharding is by sequence or head).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import torch_gen
+    from ssm_decode_amd import abi, feed, traffic
+    from ssm_decode_amd.layer import DeviceStep
+
+    abi.load()
+    dev = "cuda"
+    cfg = synth.get_config(args.workload)
+    li = synth.make_layer_inputs(cfg)
+    W = cfg.window
+    lb = traffic.config_bytes(cfg, int(li.offsets[-1]))
+
+    # ---------------------------------------------------------- layers
+    # enough instances that their sketches and rings together span at least
+    # twice the 256 MiB last-level cache
+    first = feed.make_layer(cfg, li, device=dev)
+    nonflush = first.U.nbytes + first.ring_k.nbytes + first.ring_v.nbytes + first.ring_gate.nbytes
+    L = args.layers or int(np.clip(np.ceil(2 * 256 * 2 ** 20 / nonflush), 2, 8))
+    log(f"[bench] {cfg.name}: B={cfg.batch} H={cfg.heads} dk={cfg.dk} dv={cfg.dv} W={W} "
+        f"R={int(li.offsets[-1])} layers={L} (sketch+ring {nonflush / 1e6:.0f} MB each)")
+    layers = []
+    for l in range(L):
+        lay = first if l == 0 else feed.make_layer(cfg, li, device=dev)
+        if l == 0:
+            feed.fill_state(lay, cfg, numpy_all=False)
+        else:
+            lay.S.copy_(layers[0].S)
+        assert feed.prime(lay, li) == 0
+        layers.append(lay)
+    torch.cuda.synchronize()
+    log(f"[bench] layers ready ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
+
+    # -------------------------------------------------- step input pool
+    P = max(1, args.pool)
+    pool = []
+    for t in range(P):
+        st = layers[0].new_step()
+        q, k, v, gate, beta = torch_gen.step_inputs(cfg, t, dev)
+        st.q.copy_(q); st.k.copy_(k); st.v.copy_(v); st.gate.copy_(gate)
+        if beta is not None:
+            st.beta.copy_(beta)
+        pool.append(st)
+    # one output buffer per layer
+    outs = [layers[0].new_step().o for _ in range(L)]
+    steps_structs = []
+    for t in range(P):
+        row = []
+        for l in range(L):
+            s = pool[(t + l) % P]
+            row.append(DeviceStep(s.q, s.k, s.v, s.gate, s.beta, outs[l]).struct())
+        steps_structs.append(row)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    phase = int(li.phase[0])
+    ragged = cfg.ragged
+
+    def one_step(t, ev=None, stream_handle=None):
+        sh_ = sh if stream_handle is None else stream_handle
+        due = ragged or ((t - phase) % W == 0)
+        for l, lay in enumerate(layers):
+            st = steps_structs[t % P][l]
+            if ev is not None:
+                ev["read"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                ev["read"][-1][0].record(stream)
+            rc = abi.sketchssm_read(lay.layer_struct, lay.buffers_struct, st, sh_)
+            if ev is not None:
+                ev["read"][-1][1].record(stream)
+            assert rc == 0
+            if due:
+                if ev is not None:
+                    ev["flush"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                    ev["flush"][-1][0].record(stream)
+                rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
+                                         abi.SKSSM_FLUSH_DUE, sh_)
+                if ev is not None:
+                    ev["flush"][-1][1].record(stream)
+                assert rc == 0
+
+    # the timed region starts at a window boundary
+    t = 0
+    for _ in range(args.warmup):
+        one_step(t)
+        t += 1
+    while (t - phase - 1) % W != 0 and not ragged:
+        one_step(t)
+        t += 1
+    torch.cuda.synchronize()
+
+    # ---- per-kernel durations: eager launches bracketed by HIP events on
+    # the launch stream, over two windows
+    ev = {"read": [], "flush": []}
+    for i in range(2 * W):
+        one_step(t + i, ev)
+    torch.cuda.synchronize()
+    t += 2 * W
+    read_us = [a.elapsed_time(b) * 1000 for a, b in ev["read"]]
+    flush_us = [a.elapsed_time(b) * 1000 for a, b in ev["flush"]]
+    flush_avg = float(np.mean(flush_us)) if flush_us else float("nan")
+    read_avg = float(np.mean(read_us))
+
+    # ---- the timed steps: exactly K steps (every layer's read, and its flush
+    # when a window closes) captured in one HIP graph and replayed once, so
+    # that host launch overhead is not timed; the device ring counts advance
+    # exactly as in eager execution
+    K = args.steps
+
+    def realign():
+        nonlocal t
+        while (t - phase - 1) % W != 0 and not ragged:
+            one_step(t)
+            t += 1
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        capture_handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(K):
+            one_step(t + i, stream_handle=capture_handle)
+    torch.cuda.synchronize()
+    graph.replay()                      # warm replay
+    torch.cuda.synchronize()
+    t += K
+    realign()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t += K
+    total_ms = start.elapsed_time(stop)
+    us_per_step = total_ms * 1000.0 / (K * L)
+    err = max(lay.error_word() for lay in layers)
+    assert err == 0, f"device error word {err}"
+    log(f"[bench] sketch: {us_per_step:.2f} us/step/layer (graph of {K} steps x {L} layers); "
+        f"flush avg {flush_avg:.1f} us ({len(flush_us)} launches); read avg {read_avg:.2f} us")
+
+    achieved_gbs = lb.per_step / (us_per_step * 1e-6) / 1e9
+    flush_gbs = lb.flush_launch / (flush_avg * 1e-6) / 1e9
+    read_gbs = lb.read_launch_avg / (read_avg * 1e-6) / 1e9
+    windows_exact = ragged or K % W == 0
+
+    # ------------------------------------------------ GPU baselines
+    baselines = None
+    if not args.no_baselines:
+        lay = layers[0]
+        # standard full-state step
+        nb = max(W, 16)
+        for i in range(4):
+            abi.sketchssm_full_step(lay.layer_struct, lay.buffers_struct, steps_structs[i % P][0], sh)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(nb):
+            assert abi.sketchssm_full_step(lay.layer_struct, lay.buffers_struct,
+                                           steps_structs[i % P][0], sh) == 0
+        b.record(stream)
+        torch.cuda.synchronize()
+        full_us = a.elapsed_time(b) * 1000 / nb
+        # ReplaySSM over whole windows (its ring restarts from an empty window)
+        lay.count.zero_()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(nb):
+            assert abi.sketchssm_replay_step(lay.layer_struct, lay.buffers_struct,
+                                             steps_structs[i % P][0], sh) == 0
+        b.record(stream)
+        torch.cuda.synchronize()
+        replay_us = a.elapsed_time(b) * 1000 / nb
+        baselines = {
+            "full_step_us": round(full_us, 2),
+            "full_step_gbs": round(lb.full_step / (full_us * 1e-6) / 1e9, 1),
+            "replay_step_us": round(replay_us, 2),
+            "replay_step_gbs": round(lb.replay_per_step / (replay_us * 1e-6) / 1e9, 1),
+            "speedup_vs_full": round(full_us / us_per_step, 3),
+            "speedup_vs_replay": round(replay_us / us_per_step, 3),
+        }
+        log(f"[bench] baselines: {baselines}")
+
+    # ------------------------------------------ copy-bandwidth reference
+    nbytes = 2 * 2 ** 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nbytes * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] copy bandwidth {copy_gbs:.0f} GB/s")
+
+    # ------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, li, min(args.cpu_seqs, cfg.batch), args.cpu_windows)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    result = {
+        "metric": "per-layer decode step us (W-amortised) + achieved HBM GB/s vs peak, batch 320",
+        "value": round(us_per_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "family": cfg.family, "batch": cfg.batch, "heads": cfg.heads,
+            "qk_groups": cfg.qk_groups, "dk": cfg.dk, "dv": cfg.dv, "window": W,
+            "mean_rank": cfg.mean_rank, "state": "f32", "act": cfg.act, "sketch": cfg.sketch,
+            "layers_rotated": L, "windows_exact": windows_exact,
+        },
+        "achieved_gbs": round(achieved_gbs, 1),
+        "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "frac_of_copy_bw": round(achieved_gbs / copy_gbs, 4),
+        "copy_gbs": round(copy_gbs, 1),
+        "tokens_per_s_per_layer": round(cfg.batch / (us_per_step * 1e-6), 1),
+        "algorithmic_bytes_per_step": int(round(lb.per_step)),
+        "kernels": {
+            "flush_us": round(flush_avg, 2), "flush_launches": len(flush_us),
+            "flush_bytes": lb.flush_launch, "flush_gbs": round(flush_gbs, 1),
+            "read_us": round(read_avg, 2), "read_launches": len(read_us),
+            "read_bytes_avg": int(round(lb.read_launch_avg)), "read_gbs": round(read_gbs, 1),
+            "timing": "eager launches bracketed by HIP events on the launch stream",
+        },
+        "step_timing": "the K timed steps captured in one HIP graph and replayed; "
+                       "HIP events around the replay",
+        "roofline": {
+            "bound": "hbm", "kernel": "flush", "achieved": round(flush_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
+            "traffic": TRAFFIC.get(cfg.name),
+        },
+        "baselines": baselines,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+# HBM bytes per flush launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+# by the copy-kernel calibration; None until counters are taken for the
+# current kernel.
+TRAFFIC = {}
+
+
+def cpu_baseline(cfg, li, n_seq, windows):
+    """The oracle, as it stands, on a bounded sample: n_seq sequences x every
+    head of the workload, whole windows (prime excluded), on all host cores;
+    scaled to the whole batch per layer step."""
+    import numpy as np
+    import oracle
+    import synth
+    seqs = np.arange(n_seq)
+    tiles = np.array([(b, h) for b in seqs for h in range(cfg.heads)], dtype=np.int64)
+    S0 = synth.initial_state(cfg, b_idx=seqs).reshape(-1, cfg.dk, cfg.dv)
+    orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, cfg.window, li.ranks, li.offsets, li.Pt,
+                             li.C, li.A, tiles, S0, cfg.heads, cfg.qk_groups, state_store="f32",
+                             sketch_store=cfg.sketch, out_store=cfg.act)
+    orc.flush(None, all_tiles=True)
+    orc.count[:] = li.count0[tiles[:, 0], tiles[:, 1]]
+    nsteps = windows * cfg.window
+    steps = [synth.make_step_inputs(cfg, t, b_idx=seqs) for t in range(nsteps)]
+    t0 = time.perf_counter()
+    for st in steps:
+        o = np.zeros((len(tiles), cfg.dv))
+        orc.read(st, o=o)
+        if (orc.count == cfg.window).any():
+            orc.flush(st, o=o)
+    dt = time.perf_counter() - t0
+    frac = cfg.batch / n_seq
+    us = dt / nsteps * frac * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.batch} sequences x {cfg.heads} heads, {windows} windows of "
+                      f"{cfg.window} steps ({dt:.1f} s), scaled to the batch",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -21,28 +21,30 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 SOURCES = ["sk_api.cpp", "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + CFLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    """Compile every source for gfx950 and link the shared library."""
+def build(jobs: int = 4, extra=(), out: str = LIB) -> str:
+    """Compile every source for gfx950 and link the shared library.
+    extra: additional compiler flags (e.g. -D tuning macros); out: library path."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if out == LIB else "_" + os.path.basename(out).replace(".so", "")
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, extra, tag), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -6,6 +6,8 @@
 
 namespace sk {
 
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
 typedef uint16_t bf16;  // storage type of bfloat16 values
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -56,6 +58,97 @@ __device__ __forceinline__ void st4(bf16* p, const float (&x)[4]) {
 
 template <typename T>
 __device__ __forceinline__ void st(T* p, float x) { *p = Store<T>::cvt(x); }
+
+// N consecutive elements (N in {1, 2, 4, 8}) as fp32, with the widest loads
+// the alignment of an N-element run allows.
+template <int N>
+__device__ __forceinline__ void ldn(const float* p, float (&x)[N]) {
+  if constexpr (N == 1) {
+    x[0] = p[0];
+  } else if constexpr (N == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x; x[1] = v.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + e);
+      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void ldn(const bf16* p, float (&x)[N]) {
+  if constexpr (N == 1) {
+    x[0] = to_f32(p[0]);
+  } else if constexpr (N == 2) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = __uint_as_float(v << 16); x[1] = __uint_as_float(v & 0xffff0000u);
+  } else if constexpr (N == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xffff0000u);
+    x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + e);
+      x[e] = __uint_as_float(v.x << 16); x[e + 1] = __uint_as_float(v.x & 0xffff0000u);
+      x[e + 2] = __uint_as_float(v.y << 16); x[e + 3] = __uint_as_float(v.y & 0xffff0000u);
+      x[e + 4] = __uint_as_float(v.z << 16); x[e + 5] = __uint_as_float(v.z & 0xffff0000u);
+      x[e + 6] = __uint_as_float(v.w << 16); x[e + 7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stn(float* p, const float (&x)[N]) {
+  if constexpr (N == 1) {
+    p[0] = x[0];
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 4)
+      *reinterpret_cast<float4*>(p + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+  }
+}
+template <int N>
+__device__ __forceinline__ void stn(bf16* p, const float (&x)[N]) {
+  if constexpr (N == 1) {
+    p[0] = f32_to_bf16(x[0]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      uint2 v;
+      v.x = (uint32_t)f32_to_bf16(x[e]) | ((uint32_t)f32_to_bf16(x[e + 1]) << 16);
+      v.y = (uint32_t)f32_to_bf16(x[e + 2]) | ((uint32_t)f32_to_bf16(x[e + 3]) << 16);
+      *reinterpret_cast<uint2*>(p + e) = v;
+    }
+  }
+}
+
+// N consecutive elements kept in their storage type (bf16 stays packed two
+// per register until used).
+template <typename T, int N>
+struct alignas(sizeof(T) * N) VecN {
+  T v[N];
+};
+template <int N, typename T>
+__device__ __forceinline__ VecN<T, N> ldraw(const T* p) {
+  return *reinterpret_cast<const VecN<T, N>*>(p);
+}
+template <typename T, int N>
+__device__ __forceinline__ float vget(const VecN<T, N>& x, int e) { return to_f32(x.v[e]); }
+
+// Raw copy of N consecutive elements (ring appends).
+template <int N, typename T>
+__device__ __forceinline__ void copyn(T* dst, const T* src) {
+  float x[N];
+  ldn<N>(src, x);
+  stn<N>(dst, x);
+}
+
 
 // Sum of x over the lanes that differ in lane bits [LB, LB+NB); every lane
 // receives the total.

@@ -7,25 +7,36 @@
 
 namespace sk {
 
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
+static int launch_tile(int mode, const Params& p, hipStream_t st) {
+  const size_t lds = TileLds<FAM, DK, DV, WMAX>::BYTES;
+  const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
+  if (mode == MODE_FLUSH)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX>), grid, block, lds, st, p);
+  else if (mode == MODE_FULL)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX>), grid, block, lds, st, p);
+  else if (mode == MODE_REPLAY)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX>), grid, block, lds, st, p);
+  else
+    return -4;
+  return 0;
+}
+
 template <int FAM, int DK, int DV, typename AT, typename UT>
 static int launch_shape(int mode, const Params& p, hipStream_t st) {
   if (p.B <= 0 || p.H <= 0) return 0;
   if (mode == MODE_READ) {
-    if (FAM == FAM_M2)
-      hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT>), dim3(p.B * p.G), dim3(M2R_THREADS), 0, st, p);
-    else
+    if (FAM == FAM_M2) {
+      if (p.W <= 16)
+        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 16>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
+      else
+        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 32>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
+    } else
       hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT>), dim3(p.B * p.H), dim3(64), 0, st, p);
+  } else if (p.W <= 16) {
+    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 16>(mode, p, st)) return rc;
   } else {
-    const size_t lds = sizeof(float) * tile_lds_floats<FAM, DK, DV>(p.W);
-    const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
-    if (mode == MODE_FLUSH)
-      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH>), grid, block, lds, st, p);
-    else if (mode == MODE_FULL)
-      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL>), grid, block, lds, st, p);
-    else if (mode == MODE_REPLAY)
-      hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY>), grid, block, lds, st, p);
-    else
-      return -4;
+    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 32>(mode, p, st)) return rc;
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -9,160 +9,212 @@
 namespace sk {
 
 // ---------------------------------------------------------------- Mamba-2
-// One workgroup per (sequence, B/C group).  The group's heads share k and q,
-// so the dot products d_i = k_i . q and the coefficient rows of the whole
-// group are formed once per workgroup.  For head h with n entries (the
-// step's own entry last):
+// One workgroup per (sequence, B/C group), LPH lanes per head of the group.
+// The group's heads share k and q, so the dot products d_i = k_i . q are
+// formed once per workgroup.  For head h with n entries (the step's own
+// entry last):
 //   q~ = D q, D = prod_i a_i;   o_buf = sum_i w_i d_i v_i, w_i = dt_i prod_{t>i} a_t
 //   o  = D * U_h (C_h q) + o_buf
-constexpr int M2R_THREADS = 256;
+// Lane s of a head holds: the q/k segment s (DK/LPH elements) for the dot
+// products, coefficient row j = s / (LPH/16) after the reduction, ring
+// slots s*SPL.. for the decay scan, and output columns s*CPL.. .  Every
+// global load is issued right after the ring count is known; sketch rows and
+// ring values stay packed (bf16) in registers until used.
 constexpr int M2R_MAXHPG = 16;     // heads per group handled by one workgroup
-constexpr int M2R_MAXW = 32;
+#ifndef SK_M2R_LPH
+#define SK_M2R_LPH 16              // lanes per head
+#endif
+constexpr int M2R_LPH = SK_M2R_LPH;
 
-template <int DK, int DV, typename AT, typename UT>
-__global__ void __launch_bounds__(M2R_THREADS) m2_read_kernel(Params p) {
-  constexpr int NT = M2R_THREADS;
-  __shared__ float s_q[DK];
-  __shared__ float s_d[M2R_MAXW];                       // d_i = k_i . q
-  __shared__ float s_a[M2R_MAXHPG][M2R_MAXW];           // a_i per head
-  __shared__ float s_w[M2R_MAXHPG][M2R_MAXW];           // w_i d_i per head
-  __shared__ float s_D[M2R_MAXHPG];
-  __shared__ float s_c[M2R_MAXHPG * 16];                // C_h q for the group's rows
-  __shared__ int s_n0, s_bad;
+// lanes per head for a head shape (at least one key element and one output
+// column per lane)
+template <int DK, int DV>
+struct M2ReadLanes {
+  static constexpr int v0 = M2R_LPH < DK ? M2R_LPH : DK;
+  static constexpr int LPH = v0 < DV ? v0 : DV;
+};
+
+template <int DK, int DV, typename AT, typename UT, int WMAX>
+__global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_read_kernel(Params p) {
+  constexpr int LPH = M2ReadLanes<DK, DV>::LPH;
+  constexpr int LB = ilog2c(LPH);
+  constexpr int SEG = DK / LPH;                  // key / query elements per lane
+  constexpr int CPL = DV / LPH;                  // output columns per lane
+  constexpr int SPL = WMAX >= LPH ? WMAX / LPH : 1;  // ring slots per lane in the decay scan
+  static_assert(SEG >= 1 && CPL >= 1, "head dims too small for the lane split");
+  __shared__ float s_d[WMAX];                    // d_i = k_i . q
+  __shared__ float s_c[M2R_MAXHPG * 16];         // C_h q for the group's coefficient rows
 
   const int tid = threadIdx.x;
+  const int hh = tid >> LB;                      // head within the group
+  const int s = tid & (LPH - 1);
   const int W = p.W, HPG = p.HPG;
   const int b = blockIdx.x / p.G;
   const int g = blockIdx.x - b * p.G;
   const int h0 = g * HPG;
-  const size_t bh0 = (size_t)b * p.H + h0;
+  const int h = h0 + hh;
+  const size_t bg = (size_t)b * p.G + g;
+  const size_t bh = (size_t)b * p.H + h;
 
-  if (tid == 0) {
-    const int n0 = p.count[bh0];
-    int bad = (n0 < 0 || n0 >= W) ? ERRBIT_COUNT : 0;
-    for (int hh = 1; hh < HPG; ++hh)
-      if (p.count[bh0 + hh] != n0) bad |= ERRBIT_GROUP;
-    s_n0 = n0;
-    s_bad = bad;
-    if (bad) atomicOr(p.err, bad);
+  // ---------------------------------------------------- ring counts
+  const int n0 = p.count[(size_t)b * p.H + h0];
+  const int mine = p.count[bh];
+  int bad = (n0 < 0 || n0 >= W) ? ERRBIT_COUNT : 0;
+  if (mine != n0) bad |= ERRBIT_GROUP;
+  const int off = p.off[h];
+  const int r = p.off[h + 1] - off;
+  const float Ah = p.A[h];
+  if (__syncthreads_or(bad)) {
+    if (s == 0 && bad) atomicOr(p.err, bad);
+    return;
   }
-  __syncthreads();
-  if (s_bad) return;
-  const int n0 = s_n0;
   const int n = n0 + 1;
 
-  const AT* q = reinterpret_cast<const AT*>(p.q) + ((size_t)b * p.G + g) * DK;
-  const AT* kin = reinterpret_cast<const AT*>(p.k) + ((size_t)b * p.G + g) * DK;
-  const AT* vin = reinterpret_cast<const AT*>(p.v) + bh0 * DV;
-  const AT* dtin = reinterpret_cast<const AT*>(p.gate) + bh0;
-  const AT* ring_k = reinterpret_cast<const AT*>(p.rk) + ((size_t)b * p.G + g) * W * DK;
-  const AT* ring_v = reinterpret_cast<const AT*>(p.rv) + bh0 * W * DV;   // head hh at + hh*W*DV
-  const AT* ring_dt = reinterpret_cast<const AT*>(p.rg) + bh0 * W;       // head hh at + hh*W
+  const AT* q = reinterpret_cast<const AT*>(p.q) + bg * DK;
+  const AT* kin = reinterpret_cast<const AT*>(p.k) + bg * DK;
+  const AT* vin = reinterpret_cast<const AT*>(p.v) + bh * DV;
+  const AT* dtin = reinterpret_cast<const AT*>(p.gate) + bh;
+  const AT* ring_k = reinterpret_cast<const AT*>(p.rk) + bg * W * DK;
+  const AT* ring_v = reinterpret_cast<const AT*>(p.rv) + bh * W * DV;
+  const AT* ring_dt = reinterpret_cast<const AT*>(p.rg) + bh * W;
+
+  if (n < W) {
+    // ---------------------------------------------- issue the loads
+    // sketch rows and ring values (HBM) first; they stay packed until used
+    VecN<UT, CPL> us[16];
+    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < r) us[j] = ldraw<CPL>(Ur + (size_t)j * DV);
+    // ring values of the earlier entries (constant row stride), then the step's own
+    VecN<AT, CPL> vs[WMAX];
+    const AT* rv0 = ring_v + s * CPL;
+#pragma unroll
+    for (int i = 0; i < WMAX - 1; ++i)
+      if (i < n0) vs[i] = ldraw<CPL>(rv0 + (size_t)i * DV);
+    const VecN<AT, CPL> vcur = ldraw<CPL>(vin + s * CPL);
+    float dts[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int i = s * SPL + u;
+      dts[u] = (i < n) ? ld((i == n0) ? dtin : ring_dt + i) : 0.f;
+    }
+    // d_i = k_i . q, slots spread over the group's heads (LPH lanes per slot)
+    {
+      float qs[SEG];
+      ldn<SEG>(q + s * SEG, qs);
+      for (int i = hh; i < n; i += HPG) {
+        float ks[SEG];
+        ldn<SEG>(((i == n0) ? kin : ring_k + (size_t)i * DK) + s * SEG, ks);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) d += ks[e] * qs[e];
+        d = xsum<0, LB>(d);
+        if (s == 0) s_d[i] = d;
+      }
+    }
+    // coefficient rows of the whole group, C q, RT lanes per row (L2 resident)
+    {
+      constexpr int RT = 8;                       // lanes per coefficient row
+      constexpr int RSEG = DK / RT;               // elements per lane
+      const int roff0 = p.off[h0];
+      const int rows = p.off[h0 + HPG] - roff0;
+      const int nthreads = LPH * HPG;
+      const int sg = tid & (RT - 1);
+      const VecN<AT, RSEG> qr = ldraw<RSEG>(q + sg * RSEG);
+      for (int base = 0; base < rows; base += nthreads / RT) {
+        const int row = base + tid / RT;
+        float c = 0.f;
+        if (row < rows) {
+          float cr[RSEG];
+          ldn<RSEG>(p.C + (size_t)(roff0 + row) * DK + sg * RSEG, cr);
+#pragma unroll
+          for (int e = 0; e < RSEG; ++e) c += cr[e] * vget(qr, e);
+        }
+        c = xsum<0, 3>(c);
+        if (row < rows && sg == 0) s_c[row] = c;
+      }
+    }
+    // -------------------------------- decays: suffix products per head
+    float a[SPL], lp = 1.f;
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int i = s * SPL + u;
+      a[u] = (i < n) ? m2_decay(dts[u], Ah) : 1.0f;
+      lp *= a[u];
+    }
+    float incl = lp;                               // prod over lanes >= s
+#pragma unroll
+    for (int d = 1; d < LPH; d <<= 1) {
+      const float o = __shfl_down(incl, d, LPH);
+      if (s + d < LPH) incl *= o;
+    }
+    // shuffle with every lane active (a disabled source lane reads as zero)
+    const float nxt = __shfl_down(incl, 1, LPH);
+    const float after = (s + 1 < LPH) ? nxt : 1.0f;   // prod over lanes > s
+    const float D = __shfl(incl, 0, LPH);
+    float w[SPL];
+    {
+      float suf = after;
+#pragma unroll
+      for (int u = SPL - 1; u >= 0; --u) {
+        w[u] = dts[u] * suf;                        // dt_i prod_{t>i} a_t
+        suf *= a[u];
+      }
+    }
+    __syncthreads();                               // s_d and s_c complete
+    float e[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int i = s * SPL + u;
+      e[u] = (i < n) ? w[u] * s_d[i] : 0.f;
+    }
+
+    // ------------------------------------------------------- output
+    float acc[CPL], ob[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = ob[c] = 0.f;
+    const float* cme = s_c + (off - p.off[h0]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < r) {
+        const float cj = cme[j];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += cj * vget(us[j], c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WMAX - 1; ++i) {
+      const float ei = __shfl(e[i % SPL], i / SPL, LPH);
+      if (i < n0)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ob[c] += ei * vget(vs[i], c);
+    }
+    {
+      float ecur = e[0];
+#pragma unroll
+      for (int u = 1; u < SPL; ++u)
+        if (n0 % SPL == u) ecur = e[u];
+      ecur = __shfl(ecur, n0 / SPL, LPH);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ob[c] += ecur * vget(vcur, c);
+    }
+    float out[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
+    stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
+  } else {
+    __syncthreads();                               // pairs with the barrier above
+  }
 
   // ------------------------------------------------------------ append
-  {
-    AT* rk = reinterpret_cast<AT*>(p.rk) + (((size_t)b * p.G + g) * W + n0) * DK;
-    for (int e = tid; e < DK; e += NT) rk[e] = kin[e];
-    AT* rv = reinterpret_cast<AT*>(p.rv);
-    for (int e = tid; e < HPG * DV; e += NT) {
-      const int hh = e / DV, c = e - hh * DV;
-      rv[((bh0 + hh) * W + n0) * DV + c] = vin[e];
-    }
-    AT* rdt = reinterpret_cast<AT*>(p.rg);
-    for (int hh = tid; hh < HPG; hh += NT) {
-      rdt[(bh0 + hh) * W + n0] = dtin[hh];
-      p.count[bh0 + hh] = (n == W) ? W : n;
-    }
-  }
-  if (n == W) return;        // the flush writes this step's output
-
-  // ---------------------------------------------- query and dot products
-  for (int m = tid; m < DK; m += NT) s_q[m] = ld(q + m);
-  __syncthreads();
-  {
-    // slot i handled by 16 lanes, each a DK/16 segment
-    constexpr int SEG = DK / 16;
-    for (int base = 0; base < n; base += NT / 16) {
-      const int i = base + tid / 16;
-      const int sg = tid & 15;
-      float d = 0.f;
-      if (i < n) {
-        const AT* k = (i == n0) ? kin : ring_k + (size_t)i * DK;
-#pragma unroll
-        for (int e = 0; e < SEG; ++e) d += ld(k + sg * SEG + e) * s_q[sg * SEG + e];
-      }
-      d = xsum<0, 4>(d);
-      if (i < n && sg == 0) s_d[i] = d;
-    }
-  }
-  // ------------------------------------------------------ decays a_i
-  for (int idx = tid; idx < HPG * n; idx += NT) {
-    const int hh = idx / n, i = idx - hh * n;
-    const float dt = (i == n0) ? ld(dtin + hh) : ld(ring_dt + (size_t)hh * W + i);
-    s_a[hh][i] = m2_decay(dt, p.A[h0 + hh]);
-  }
-  // ----------------------------------------- coefficient rows c = C_h q
-  const int roff0 = p.off[h0];
-  const int rows = p.off[h0 + HPG] - roff0;
-  {
-    constexpr int SEG = DK / 4;
-    for (int base = 0; base < rows; base += NT / 4) {
-      const int row = base + tid / 4;
-      const int sg = tid & 3;
-      float c = 0.f;
-      if (row < rows) {
-        const float* Cr = p.C + (size_t)(roff0 + row) * DK + sg * SEG;
-#pragma unroll
-        for (int e = 0; e < SEG; e += 4) {
-          const float4 cv = *reinterpret_cast<const float4*>(Cr + e);
-          c += cv.x * s_q[sg * SEG + e] + cv.y * s_q[sg * SEG + e + 1] +
-               cv.z * s_q[sg * SEG + e + 2] + cv.w * s_q[sg * SEG + e + 3];
-        }
-      }
-      c = xsum<0, 2>(c);
-      if (row < rows && sg == 0) s_c[row] = c;
-    }
-  }
-  __syncthreads();
-  // ------------------------- weights w_i d_i = dt_i prod_{t>i} a_t d_i, D
-  for (int idx = tid; idx < HPG * n; idx += NT) {
-    const int hh = idx / n, i = idx - hh * n;
-    float suf = 1.f;
-    for (int t = i + 1; t < n; ++t) suf *= s_a[hh][t];
-    const float dt = (i == n0) ? ld(dtin + hh) : ld(ring_dt + (size_t)hh * W + i);
-    s_w[hh][i] = dt * suf * s_d[i];
-    if (i == 0) s_D[hh] = s_a[hh][0] * suf;
-  }
-  __syncthreads();
-
-  // ------------------------------------------------------------ output
-  constexpr int CG = DV / 4;
-  for (int idx = tid; idx < HPG * CG; idx += NT) {
-    const int hh = idx / CG, c4 = (idx - hh * CG) * 4;
-    const int h = h0 + hh;
-    const int off = p.off[h], r = p.off[h + 1] - off;
-    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + c4;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < r; ++j) {
-      float u[4];
-      ld4(Ur + (size_t)j * DV, u);
-      const float cj = s_c[off - roff0 + j];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += cj * u[c];
-    }
-    const float D = s_D[hh];
-    float ob[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < n; ++i) {
-      float v[4];
-      ld4((i == n0) ? vin + (size_t)hh * DV + c4 : ring_v + ((size_t)hh * W + i) * DV + c4, v);
-      const float wd = s_w[hh][i];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ob[c] += wd * v[c];
-    }
-    float out[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) out[c] = D * acc[c] + ob[c];
-    st4(reinterpret_cast<AT*>(p.o) + (bh0 + hh) * DV + c4, out);
+  AT* rk = reinterpret_cast<AT*>(p.rk) + (bg * W + n0) * DK;
+  AT* rv = reinterpret_cast<AT*>(p.rv) + (bh * W + n0) * DV;
+  if (hh == 0) copyn<SEG>(rk + s * SEG, kin + s * SEG);
+  copyn<CPL>(rv + s * CPL, vin + s * CPL);
+  if (s == 0) {
+    reinterpret_cast<AT*>(p.rg)[bh * W + n0] = dtin[0];
+    p.count[bh] = n;
   }
 }
 

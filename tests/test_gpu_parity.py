@@ -143,3 +143,40 @@ def test_full_stress_sweep(idx):
     steps = cfg.steps if (cfg.window, cfg.mean_rank) == (16, 8) else 2 * cfg.window + 7
     tiles = sample_tiles(cfg, 4, 3, seed=cfg.seed)
     run(cfg, "sketch", steps=steps, tiles=tiles, numpy_all=False)
+
+
+@pytest.mark.parametrize("name,W", [("m2_b320", 16), ("m2_b320", 32), ("gdn_b256", 16), ("kda_b256", 32)])
+def test_read_at_every_ring_fill(name, W):
+    """One sketched read from every ring fill n0 = 0..W-2 (identity-padded
+    ring), so every lane position of the slot scans and broadcasts holds the
+    step's own entry once."""
+    import synth
+    import oracle
+    from ssm_decode_amd import feed
+    from tests.gpu_parity import rel_l2, all_tiles, tol_out
+    cfg = CONFIGS[name].with_(name=f"{name}_fill", batch=1, window=W)
+    li = synth.make_layer_inputs(cfg)
+    tiles = all_tiles(cfg)
+    S0 = synth.initial_state(cfg).reshape(-1, cfg.dk, cfg.dv)
+    worst = 0.0
+    for n0 in range(W - 1):
+        lay = feed.make_layer(cfg, li)
+        feed.fill_state(lay, cfg, numpy_all=True)
+        assert feed.prime(lay, li) == 0
+        orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, W, li.ranks, li.offsets, li.Pt, li.C,
+                                 li.A, tiles, S0, cfg.heads, cfg.qk_groups, state_store="f32",
+                                 sketch_store=cfg.sketch, out_store=cfg.act)
+        orc.flush(None, all_tiles=True)
+        lay.count.fill_(n0)
+        orc.count[:] = n0
+        step = lay.new_step()
+        feed.fill_step(step, cfg, 0, numpy_all=True)
+        assert lay.read(step) == 0
+        torch.cuda.synchronize()
+        o_ref = np.zeros((len(tiles), cfg.dv))
+        orc.read(synth.make_step_inputs(cfg, 0), o=o_ref)
+        e = rel_l2(step.o.float().cpu().numpy().reshape(-1, cfg.dv), o_ref)
+        worst = max(worst, e)
+        assert e <= tol_out(cfg), (n0, e)
+        assert (lay.count.cpu().numpy() == n0 + 1).all()
+    print(f"  {name} W={W}: every ring fill, max rel-L2 {worst:.2e}")
