@@ -5,7 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/sketchssm.h"
+#include "sketchssm.h"
 #include "sk_params.hpp"
 
 namespace {

@@ -5,17 +5,24 @@
 // query / basis vectors and stored once.
 //
 // Register layout.  The dv columns are split into column blocks of CB = 64
-// (or dv when smaller), one wave per block.  Lane l owns the four columns
-// 4*cg..4*cg+3 of its block (cg = l % NCG) and the rows m = rg + NRG*j,
-// j = 0..RPL-1 (rg = l / NCG).  Reductions over rows (S^T x for the query,
-// the basis vectors, the delta-rule key) are in-lane sums over j followed by
-// an exchange across the NRG lanes that share cg.
+// (or dv when smaller), one wave per block.  With cg = lane % 16 and
+// rg = lane / 16, lane l holds the NCC = CB/16 consecutive columns
+// NCC*cg .. NCC*cg+NCC-1 of its block and, for every 16-row block mb, the four
+// consecutive rows 16*mb + 4*rg + v (v = 0..3):
+//     sacc[mb][c][v] = S[16 mb + 4 rg + v][NCC cg + c]
+// This is at once
+//   - the accumulator layout of v_mfma_f32_16x16x4_f32 (D[4 rg + v][cg]) for
+//     the 16 x 16 block (rows 16 mb.., columns NCC j + c), so the Mamba-2
+//     rank-W update S += K V'^T runs on the matrix cores with S in place, and
+//   - the A-operand layout (A[cg][rg]) of the same instruction for S^T, with
+//     K-step (mb, v) covering rows 16 mb + 4 k + v, so U = S^T P needs no
+//     data movement either;
+// and every lane's four columns of a row are one 128-bit load or store.
 //
 // Latency structure.  Every global load the tile needs besides the state
 // (ring keys, values and gates, the basis rows, the query) is issued first,
-// as 16-byte chunks spread over the workgroup, then the state's 128-bit
-// loads; the small loads are consumed (staged into LDS as fp32) while the
-// state is still in flight.
+// as 16-byte chunks spread over the workgroup, then the state loads; the
+// small loads are staged into LDS as fp32 while the state is in flight.
 #pragma once
 
 #include "sk_device.hpp"
@@ -27,25 +34,18 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int round4(int x) { return (x + 3) & ~3; }
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 template <int DK, int DV>
 struct TileShape {
   static constexpr int CB = DV >= 64 ? 64 : DV;   // columns per wave
   static constexpr int NCB = DV / CB;             // waves per tile
-  static constexpr int NCG = CB / 4;              // column groups per wave
-  static constexpr int NRG = 64 / NCG;            // row groups per wave
-  static constexpr int RPL = DK / NRG;            // rows per lane
-  static constexpr int LB = ilog2(NCG);           // lane bits of cg
-  static constexpr int NB = ilog2(NRG);           // lane bits of rg
-  static constexpr int XS = RPL + 4;              // padded per-row-group stride of a permuted vector
-  static constexpr int XLEN = NRG * XS;           // floats of one row-permuted dk-vector
-  static constexpr int PS = 20;                   // padded row stride of the staged basis (16 + 4)
+  static constexpr int NCC = CB / 16;             // consecutive columns per lane
+  static constexpr int MB = DK / 16;              // 16-row blocks
   static constexpr int THREADS = 64 * NCB;
-  static_assert(RPL >= 1 && DK % NRG == 0, "unsupported dk/dv");
+  static constexpr int PS = 20;                   // padded row stride of the staged basis (16 + 4)
+  static_assert(DK % 16 == 0 && (NCC == 2 || NCC == 4), "unsupported dk/dv");
   static_assert(DV % CB == 0, "unsupported dv");
-  static_assert(NRG >= 4 && NRG <= 16, "row groups must number 4..16");
-
-  // position of row m in a row-permuted vector (lane rg reads XS-strided runs)
-  static __host__ __device__ constexpr int perm(int m) { return (m % NRG) * XS + m / NRG; }
 };
 
 // LDS layout of a tile kernel (offsets in floats).
@@ -53,20 +53,21 @@ template <int FAM, int DK, int DV, int WMAX>
 struct TileLds {
   using T = TileShape<DK, DV>;
   static constexpr int KWS = WMAX + 4;                         // Mamba-2 key row stride ([m][slot])
-  static constexpr int Q = 0;                                  // query, permuted
-  static constexpr int QT = Q + T::XLEN;                       // effective query, permuted
-  static constexpr int SA = QT + T::XLEN;                      // per-slot scalars
+  static constexpr int Q = 0;                                  // query [dk]
+  static constexpr int QT = Q + DK;                            // effective query [dk]
+  static constexpr int SA = QT + DK;                           // per-slot scalars
   static constexpr int SW = SA + WMAX;
   static constexpr int SE = SW + WMAX;
   static constexpr int SX = SE + WMAX;
   static constexpr int MISC = SX + WMAX;
   static constexpr int V = MISC + 4;                           // values [slot][dv]
-  static constexpr int BIG = V + WMAX * DV;                    // keys (and KDA gates), later the basis
-  static constexpr int KEYS = FAM == FAM_M2 ? DK * KWS : WMAX * T::XLEN * (FAM == FAM_KDA ? 2 : 1);
-  static constexpr int BASIS = DK * T::PS;
-  static constexpr int TOTAL = BIG + (KEYS > BASIS ? KEYS : BASIS);
+  static constexpr int KEYS0 = V + WMAX * DV;                  // keys: M2 [m][slot]; GDN/KDA [slot][m]
+  static constexpr int KEYS = FAM == FAM_M2 ? DK * KWS : WMAX * DK * (FAM == FAM_KDA ? 2 : 1);
+  static constexpr int BASIS = DK * T::PS;                     // basis [m][j], over the keys after the update
+  static constexpr int P0 = KEYS0;
+  static constexpr int TOTAL = KEYS0 + (KEYS > BASIS ? KEYS : BASIS);
   static constexpr int BYTES = TOTAL * 4;
-  static_assert(BIG % 4 == 0 && V % 4 == 0, "LDS regions must be 16-byte aligned");
+  static_assert(V % 4 == 0 && KEYS0 % 4 == 0 && P0 % 4 == 0, "LDS regions must be 16-byte aligned");
 };
 
 template <typename AT>
@@ -85,13 +86,18 @@ __device__ __forceinline__ void unpack(const uint4& r, float (&x)[8], const floa
   x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
 }
 
+// D += A B for one 16x16x4 fp32 block (A: lane holds A[lane%16][lane/16],
+// B: lane holds B[lane/16][lane%16], D: lane holds D[4(lane/16)+v][lane%16]).
+__device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, d, 0, 0, 0);
+}
+
 template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX>
 __global__ void __launch_bounds__((TileShape<DK, DV>::THREADS), 2)
 tile_kernel(Params p) {
   using T = TileShape<DK, DV>;
   using LY = TileLds<FAM, DK, DV, WMAX>;
-  constexpr int CB = T::CB, NCG = T::NCG, NRG = T::NRG, RPL = T::RPL;
-  constexpr int LB = T::LB, NB = T::NB, XS = T::XS, XLEN = T::XLEN, PS = T::PS;
+  constexpr int CB = T::CB, NCC = T::NCC, MB = T::MB, PS = T::PS;
   constexpr int NT = T::THREADS;
   constexpr int KWS = LY::KWS;
 
@@ -103,20 +109,21 @@ tile_kernel(Params p) {
   float* s_e = smem + LY::SE;      // ReplaySSM buffered-output coefficients
   float* s_misc = smem + LY::MISC; // [0] = M2 total decay D
   float* s_v = smem + LY::V;       // values (M2: scaled by w_i)
-  float* s_k = smem + LY::BIG;     // keys: M2 [m][slot]; GDN/KDA [slot][perm m] (+ KDA gates)
-  float* s_p = smem + LY::BIG;     // basis [m][j], after the update
+  float* s_k = smem + LY::KEYS0;   // keys: M2 [m][slot]; GDN/KDA [slot][m] (+ KDA gates)
+  float* s_p = smem + LY::P0;      // basis [m][j], staged over the keys after the update
 
   const int W = p.W;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int cg = lane % NCG;
-  const int rg = lane / NCG;
+  const int cg = lane & 15;
+  const int rg = lane >> 4;
   const int tile = blockIdx.x;
   const int b = tile / p.H;
   const int h = tile - b * p.H;
   const int g = h / p.HPG;
   const size_t bh = (size_t)b * p.H + h;
+  const int colbase = wv * CB + NCC * cg;        // first of the lane's columns
 
   // ------------------------------------------------------------ window
   int n0 = 0;                       // entries already in the ring
@@ -204,7 +211,7 @@ tile_kernel(Params p) {
       }
     }
   }
-  // basis rows (flush): r rows of DK fp32, loaded after the update
+  // basis rows (flush): r rows of DK fp32 (L2 resident), loaded after the update
   int off = 0, r = 0;
   constexpr int PCPR = DK / 4;
   constexpr int PU = cdiv(16 * PCPR, NT);
@@ -224,10 +231,19 @@ tile_kernel(Params p) {
   }
 
   // ------------------------------------------------ issue the state loads
-  const float* Sg = p.S + bh * DK * DV + wv * CB + 4 * cg;
-  float s[RPL][4];
+  f32x4v sacc[MB][NCC];
+  {
+    const float* Sg = p.S + bh * DK * DV + colbase;
 #pragma unroll
-  for (int j = 0; j < RPL; ++j) ld4(Sg + (size_t)(rg + NRG * j) * DV, s[j]);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x[NCC];
+        ldn<NCC>(Sg + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+#pragma unroll
+        for (int c = 0; c < NCC; ++c) sacc[mb][c][v] = x[c];
+      }
+  }
 
   // ------------------------------------------------ append (ReplaySSM)
   if (MODE == MODE_REPLAY) {
@@ -277,7 +293,7 @@ tile_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < cdiv(DK, NT); ++u) {
       const int m = tid + NT * u;
-      if (m < DK) s_q[T::perm(m)] = qv[u];
+      if (m < DK) s_q[m] = qv[u];
     }
   }
   // keys into LDS as fp32
@@ -291,7 +307,7 @@ tile_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < KC; ++e) {
         if (FAM == FAM_M2) s_k[(m0 + e) * KWS + i] = x[e];
-        else s_k[i * XLEN + T::perm(m0 + e)] = x[e];
+        else s_k[i * DK + m0 + e] = x[e];
       }
     }
   }
@@ -308,9 +324,7 @@ tile_kernel(Params p) {
       const int c = tid + NT * u;
       if (c < n * GCPR) {
         const int i = c / GCPR, m0 = (c - i * GCPR) * 4;
-        const float x[4] = {gr[u].x, gr[u].y, gr[u].z, gr[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_k[(WMAX + i) * XLEN + T::perm(m0 + e)] = x[e];
+        *reinterpret_cast<float4*>(s_k + (WMAX + i) * DK + m0) = gr[u];
       }
     }
   }
@@ -335,96 +349,107 @@ tile_kernel(Params p) {
   __syncthreads();
 
   float out_val = 0.0f;      // reduced output value owned by this lane
-  int out_c = 0;             // its column within the lane's group of four
+  int out_c = 0;             // its column within the lane's group of NCC
   bool out_writer = false;
-  const int colbase = wv * CB + 4 * cg;
 
   if (do_flush) {
     // -------------------------------------------- apply the entries
     if (FAM == FAM_M2) {
-      // S <- D S + sum_i k_i (w_i v_i)^T  (the Mamba-2 steps in closed form)
+      // S <- D S + sum_i k_i (w_i v_i)^T, the Mamba-2 steps in closed form, as
+      // 16x16x4 matrix products: A = keys (rows 16 mb.., slots t4..t4+3),
+      // B = scaled values (slots t4.., columns NCC j + c)
       const float D = s_misc[0];
 #pragma unroll
-      for (int j = 0; j < RPL; ++j)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s[j][c] *= D;
-      for (int sg = 0; sg < n; sg += 4) {
-        float4 v4[4];
+        for (int c = 0; c < NCC; ++c) sacc[mb][c] *= D;
+      for (int t4 = 0; t4 < n; t4 += 4) {
+        float bv[NCC];
+        ldn<NCC>(s_v + (t4 + rg) * DV + colbase, bv);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v4[u] = *reinterpret_cast<const float4*>(s_v + (sg + u) * DV + colbase);
+        for (int mb = 0; mb < MB; ++mb) {
+          const float ak = s_k[(16 * mb + cg) * KWS + t4 + rg];
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-          const float4 kq = *reinterpret_cast<const float4*>(s_k + (rg + NRG * j) * KWS + sg);
-          s[j][0] += kq.x * v4[0].x + kq.y * v4[1].x + kq.z * v4[2].x + kq.w * v4[3].x;
-          s[j][1] += kq.x * v4[0].y + kq.y * v4[1].y + kq.z * v4[2].y + kq.w * v4[3].y;
-          s[j][2] += kq.x * v4[0].z + kq.y * v4[1].z + kq.z * v4[2].z + kq.w * v4[3].z;
-          s[j][3] += kq.x * v4[0].w + kq.y * v4[1].w + kq.z * v4[2].w + kq.w * v4[3].w;
+          for (int c = 0; c < NCC; ++c) sacc[mb][c] = mfma16x4(ak, bv[c], sacc[mb][c]);
         }
       }
     } else {
       // delta rule, one entry at a time
       for (int i = 0; i < n; ++i) {
-        float kk[RPL];
-        const float* kp = s_k + i * XLEN + rg * XS;
+        float kk[MB][4];
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) kk[j] = kp[j];
+        for (int mb = 0; mb < MB; ++mb) {
+          const float4 k4 = *reinterpret_cast<const float4*>(s_k + i * DK + 16 * mb + 4 * rg);
+          kk[mb][0] = k4.x; kk[mb][1] = k4.y; kk[mb][2] = k4.z; kk[mb][3] = k4.w;
+        }
         if (FAM == FAM_KDA) {
-          const float* gp = s_k + (WMAX + i) * XLEN + rg * XS;
 #pragma unroll
-          for (int j = 0; j < RPL; ++j) {
-            const float gj = gp[j];
+          for (int mb = 0; mb < MB; ++mb) {
+            const float4 g4 = *reinterpret_cast<const float4*>(s_k + (WMAX + i) * DK + 16 * mb + 4 * rg);
+            const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[j][c] *= gj;
+            for (int c = 0; c < NCC; ++c)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) sacc[mb][c][v] *= gv[v];
           }
         }
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        float u[NCC];
 #pragma unroll
-        for (int j = 0; j < RPL; ++j)
+        for (int c = 0; c < NCC; ++c) {
+          float a = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) u[c] += s[j][c] * kk[j];
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) u[c] = xsum<LB, NB>(u[c]);
-        const float4 v4 = *reinterpret_cast<const float4*>(s_v + i * DV + colbase);
-        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+            for (int v = 0; v < 4; ++v) a += sacc[mb][c][v] * kk[mb][v];
+          u[c] = xsum<4, 2>(a);                      // over the four row groups
+        }
+        float vvv[NCC];
+        ldn<NCC>(s_v + i * DV + colbase, vvv);
         const float beta = s_w[i];
-        float dl[4];
+        float dl[NCC];
         if (FAM == FAM_GDN) {
           const float al = s_a[i];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) dl[c] = beta * (v[c] - al * u[c]);
+          for (int c = 0; c < NCC; ++c) dl[c] = beta * (vvv[c] - al * u[c]);
 #pragma unroll
-          for (int j = 0; j < RPL; ++j)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[j][c] = al * s[j][c] + kk[j] * dl[c];
+            for (int c = 0; c < NCC; ++c)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) sacc[mb][c][v] = al * sacc[mb][c][v] + kk[mb][v] * dl[c];
         } else {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) dl[c] = beta * (v[c] - u[c]);
+          for (int c = 0; c < NCC; ++c) dl[c] = beta * (vvv[c] - u[c]);
 #pragma unroll
-          for (int j = 0; j < RPL; ++j)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[j][c] += kk[j] * dl[c];
+            for (int c = 0; c < NCC; ++c)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) sacc[mb][c][v] += kk[mb][v] * dl[c];
         }
       }
     }
 
     // ------------------------------------------ exact output S^T q
     if (want_out) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      const float* qp = s_q + rg * XS;
+      float acc[NCC];
 #pragma unroll
-      for (int j = 0; j < RPL; ++j) {
-        const float qj = qp[j];
+      for (int c = 0; c < NCC; ++c) acc[c] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += s[j][c] * qj;
+      for (int mb = 0; mb < MB; ++mb) {
+        const float4 q4 = *reinterpret_cast<const float4*>(s_q + 16 * mb + 4 * rg);
+        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int c = 0; c < NCC; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[c] += sacc[mb][c][v] * qq[v];
       }
-      // four columns over NRG >= 4 row groups: halve over the top two lane
-      // bits (one column per lane), plain sums over the rest
-      constexpr int NB1 = 2;
-      constexpr int NB0 = NB - NB1;
-      tr_reduce<4, LB + NB0, NB1>(acc, lane);
-      out_val = xsum<LB, NB0>(acc[0]);
-      out_c = (lane >> (LB + NB0)) & 3;
-      out_writer = ((lane >> LB) & ((1 << NB0) - 1)) == 0;
+      // NCC columns over the four row groups: halve over the top lane bits
+      constexpr int NBH = ilog2(NCC);
+      tr_reduce<NCC, 4 + 2 - NBH, NBH>(acc, lane);
+      out_val = xsum<4, 2 - NBH>(acc[0]);
+      out_c = (lane >> (6 - NBH)) & (NCC - 1);
+      out_writer = ((lane >> 4) & ((1 << (2 - NBH)) - 1)) == 0;
     }
   } else {
     // ----------------------- ReplaySSM non-flush: exact S0^T q~ + o_buf
@@ -432,11 +457,11 @@ tile_kernel(Params p) {
       // q~ = D q ; buffered term sum_i (k_i . q) (w_i v_i)
       if (wv == 0 && lane < n) {
         float d = 0.f;
-        for (int m = 0; m < DK; ++m) d += s_k[m * KWS + lane] * s_q[T::perm(m)];
+        for (int m = 0; m < DK; ++m) d += s_k[m * KWS + lane] * s_q[m];
         s_e[lane] = d;
       }
       const float D = s_misc[0];
-      for (int m = tid; m < DK; m += NT) s_qt[T::perm(m)] = D * s_q[T::perm(m)];
+      for (int m = tid; m < DK; m += NT) s_qt[m] = D * s_q[m];
     } else if (wv == 0) {
       // serial pull-back, newest entry first: d = k_i . r ; e_i = beta_i d ;
       // r <- alpha (r - beta d k) (GDN) or g (.) (r - beta d k) (KDA)
@@ -445,7 +470,7 @@ tile_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < EK; ++e) {
         const int m = lane * EK + e;
-        r[e] = (m < DK) ? s_q[T::perm(m)] : 0.f;
+        r[e] = (m < DK) ? s_q[m] : 0.f;
       }
       for (int t = 0; t < n; ++t) {
         const int i = n - 1 - t;
@@ -454,7 +479,7 @@ tile_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < EK; ++e) {
           const int m = lane * EK + e;
-          kk[e] = (m < DK) ? s_k[i * XLEN + T::perm(m)] : 0.f;
+          kk[e] = (m < DK) ? s_k[i * DK + m] : 0.f;
           d += kk[e] * r[e];
         }
         d = xsum<0, 6>(d);
@@ -463,32 +488,34 @@ tile_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < EK; ++e) {
           const int m = lane * EK + e;
-          const float dec = (FAM == FAM_GDN) ? s_a[i]
-                                             : ((m < DK) ? s_k[(WMAX + i) * XLEN + T::perm(m)] : 0.f);
+          const float dec = (FAM == FAM_GDN) ? s_a[i] : ((m < DK) ? s_k[(WMAX + i) * DK + m] : 0.f);
           r[e] = dec * (r[e] - beta * d * kk[e]);
         }
       }
 #pragma unroll
       for (int e = 0; e < EK; ++e) {
         const int m = lane * EK + e;
-        if (m < DK) s_qt[T::perm(m)] = r[e];
+        if (m < DK) s_qt[m] = r[e];
       }
     }
     __syncthreads();
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* qp = s_qt + rg * XS;
+    float acc[NCC];
 #pragma unroll
-    for (int j = 0; j < RPL; ++j) {
-      const float qj = qp[j];
+    for (int c = 0; c < NCC; ++c) acc[c] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += s[j][c] * qj;
+    for (int mb = 0; mb < MB; ++mb) {
+      const float4 q4 = *reinterpret_cast<const float4*>(s_qt + 16 * mb + 4 * rg);
+      const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+      for (int c = 0; c < NCC; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[c] += sacc[mb][c][v] * qq[v];
     }
-    constexpr int NB1 = 2;
-    constexpr int NB0 = NB - NB1;
-    tr_reduce<4, LB + NB0, NB1>(acc, lane);
-    const float vsum = xsum<LB, NB0>(acc[0]);
-    out_c = (lane >> (LB + NB0)) & 3;
-    out_writer = ((lane >> LB) & ((1 << NB0) - 1)) == 0;
+    constexpr int NBH = ilog2(NCC);
+    tr_reduce<NCC, 4 + 2 - NBH, NBH>(acc, lane);
+    const float vsum = xsum<4, 2 - NBH>(acc[0]);
+    out_c = (lane >> (6 - NBH)) & (NCC - 1);
+    out_writer = ((lane >> 4) & ((1 << (2 - NBH)) - 1)) == 0;
     float ob = 0.f;
     for (int i = 0; i < n; ++i) ob += s_e[i] * s_v[i * DV + colbase + out_c];
     out_val = vsum + ob;
@@ -504,14 +531,21 @@ tile_kernel(Params p) {
     // ------------------------------------------------ store the state
     float* Sw = p.S + bh * DK * DV + colbase;
 #pragma unroll
-    for (int j = 0; j < RPL; ++j) {
-      const f32x4 v4 = {s[j][0], s[j][1], s[j][2], s[j][3]};
-      __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(Sw + (size_t)(rg + NRG * j) * DV));
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* dst = Sw + (size_t)(16 * mb + 4 * rg + v) * DV;
+        if constexpr (NCC == 4) {
+          const f32x4 v4 = {sacc[mb][0][v], sacc[mb][1][v], sacc[mb][2][v], sacc[mb][3][v]};
+          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(dst));
+        } else {
+          const float x[2] = {sacc[mb][0][v], sacc[mb][1][v]};
+          stn<2>(dst, x);
+        }
+      }
 
-    // --------------------------------- sketch U = S^T P (flush only)
+    // --------------------------- sketch U = S^T P on the matrix cores
     if (want_u) {
-      const int r4 = round4(r);
       float4 pr[PU];
 #pragma unroll
       for (int u = 0; u < PU; ++u) {
@@ -522,46 +556,46 @@ tile_kernel(Params p) {
           pr[u] = *reinterpret_cast<const float4*>(p.Pt + (size_t)(off + j) * DK + m0);
         }
       }
-      __syncthreads();   // keys no longer needed: stage the basis over them
+      __syncthreads();      // keys no longer needed: basis [m][j] over them, rows j >= r zero
 #pragma unroll
       for (int u = 0; u < PU; ++u) {
         const int c = tid + NT * u;
-        if (c < r4 * PCPR) {
+        if (c < 16 * PCPR) {
           const int j = c / PCPR, m0 = (c - j * PCPR) * 4;
           const float x[4] = {pr[u].x, pr[u].y, pr[u].z, pr[u].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s_p[(m0 + e) * PS + j] = (j < r) ? x[e] : 0.0f;
+          for (int e = 0; e < 4; ++e) s_p[(m0 + e) * PS + j] = x[e];
         }
       }
       __syncthreads();
-      UT* Ub = reinterpret_cast<UT*>(p.U) + ((size_t)b * p.R + off) * DV + colbase;
-      for (int ch = 0; ch < r4; ch += 4) {
-        float acc[16];
+      // column block c: D[i][j] = sum_m S[m][NCC i + c] P[m][j], K-steps (mb, v)
+      f32x4v u[NCC];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      for (int c = 0; c < NCC; ++c) u[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-          const float4 pv = *reinterpret_cast<const float4*>(s_p + (rg + NRG * j) * PS + ch);
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            acc[c * 4 + 0] += s[j][c] * pv.x;
-            acc[c * 4 + 1] += s[j][c] * pv.y;
-            acc[c * 4 + 2] += s[j][c] * pv.z;
-            acc[c * 4 + 3] += s[j][c] * pv.w;
-          }
+        for (int v = 0; v < 4; ++v) {
+          const float bp = s_p[(16 * mb + 4 * rg + v) * PS + cg];
+#pragma unroll
+          for (int c = 0; c < NCC; ++c) u[c] = mfma16x4(sacc[mb][c][v], bp, u[c]);
         }
-        constexpr int NBU = NB <= 4 ? NB : 4;
-        constexpr int NBR = NB - NBU;
-        tr_reduce<16, LB + NBR, NBU>(acc, lane);
-        constexpr int K = 16 >> NBU;
-        const int sel = (lane >> (LB + NBR)) & ((1 << NBU) - 1);
-        const bool writer = ((lane >> LB) & ((1 << NBR) - 1)) == 0;
+      // lane holds u_j, j = cg, at columns NCC (4 rg + vv) + c of its block
+      if (cg < r) {
+        UT* Ub = reinterpret_cast<UT*>(p.U) + ((size_t)b * p.R + off + cg) * DV + wv * CB + NCC * 4 * rg;
+        float x[4 * NCC];
 #pragma unroll
-        for (int e = 0; e < K; ++e) {
-          const float val = xsum<LB, NBR>(acc[e]);
-          const int idx = sel * K + e;
-          const int c = idx >> 2, jj = idx & 3;
-          if (writer && ch + jj < r) st(Ub + (size_t)(ch + jj) * DV + c, val);
+        for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+          for (int c = 0; c < NCC; ++c) x[NCC * vv + c] = u[c][vv];
+        if constexpr (NCC == 4) {
+          float x0[8], x1[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { x0[e] = x[e]; x1[e] = x[8 + e]; }
+          stn<8>(Ub, x0);
+          stn<8>(Ub + 8, x1);
+        } else {
+          stn<8>(Ub, x);
         }
       }
     }
