@@ -40,8 +40,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=16, help="device-resident step inputs cycled")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-baselines", action="store_true", help="skip full/replay GPU baselines")
-    ap.add_argument("--cpu-seqs", type=int, default=160, help="sequences in the CPU sample")
-    ap.add_argument("--cpu-windows", type=int, default=2, help="windows in the CPU sample")
+    ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
+    ap.add_argument("--cpu-windows", type=int, default=12, help="windows in the CPU sample")
     return ap.parse_args()
 
 
@@ -299,7 +299,9 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "flush", "achieved": round(flush_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
-            "traffic": TRAFFIC.get(cfg.name),
+            "traffic": flush_traffic(cfg.name),
+            "traffic_unit": "HBM bytes per flush launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
+                            "copy-calibrated); null when the flush kernel changed since",
         },
         "baselines": baselines,
         "cpu_baseline": cpu,
@@ -307,10 +309,32 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-# HBM bytes per flush launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
-# by the copy-kernel calibration; None until counters are taken for the
-# current kernel.
-TRAFFIC = {}
+# HBM bytes per flush launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
+# scaled by what the counter reads for a 2 GiB copy (FETCH_SIZE x 2.000,
+# WRITE_SIZE x 1.000), with the digest of the flush kernel's sources at the
+# time the counters were taken.  A different digest means the kernel has
+# changed since, and the figure is reported as null.
+TRAFFIC = {
+    "m2_b320": {"bytes": 2892519465,
+                "src_sha256": "0b4b12b7b87e8c0c1547989c0144bff898736958e540839230c4702c26a8efcc"},
+}
+FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
+
+
+def flush_src_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FLUSH_SOURCES:
+        with open(os.path.join(ROOT, "ssm_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def flush_traffic(name):
+    e = TRAFFIC.get(name)
+    if e is None or e["src_sha256"] != flush_src_digest():
+        return None
+    return e["bytes"]
 
 
 def cpu_baseline(cfg, li, n_seq, windows):
@@ -329,14 +353,15 @@ def cpu_baseline(cfg, li, n_seq, windows):
     orc.flush(None, all_tiles=True)
     orc.count[:] = li.count0[tiles[:, 0], tiles[:, 1]]
     nsteps = windows * cfg.window
-    steps = [synth.make_step_inputs(cfg, t, b_idx=seqs) for t in range(nsteps)]
-    t0 = time.perf_counter()
-    for st in steps:
+    dt = 0.0
+    for t in range(nsteps):
+        st = synth.make_step_inputs(cfg, t, b_idx=seqs)      # generation is not timed
         o = np.zeros((len(tiles), cfg.dv))
+        t0 = time.perf_counter()
         orc.read(st, o=o)
         if (orc.count == cfg.window).any():
             orc.flush(st, o=o)
-    dt = time.perf_counter() - t0
+        dt += time.perf_counter() - t0
     frac = cfg.batch / n_seq
     us = dt / nsteps * frac * 1e6
     return {"value": round(us, 1), "unit": "us/step", "cores": oracle.num_threads(), "kind": "oracle",
