@@ -112,6 +112,9 @@ typedef struct {
                                 0..W; every head of a sequence advances together */
   const float* A;            /* Mamba-2: [H] fp32; NULL otherwise */
   int32_t* err;              /* [1] device error word (SKSSM_ERRBIT_*), never cleared here */
+  void* work;                /* workspace of sketchssm_workspace_bytes(layer) bytes (16-byte
+                                aligned; may be NULL when that is 0); scratch that a call
+                                overwrites, so calls sharing one workspace must be ordered */
 } sketchssm_buffers;
 
 typedef struct {             /* one decode step */
@@ -128,7 +131,8 @@ typedef struct {             /* one decode step */
  * o^ = U c, plus the exact buffered contribution; paper Sec. 3.2 and
  * App. C.1 for q~).  For every tile: append the step's (k, v, gate, beta) at
  * ring slot count, count += 1; if count < W write o = U (C q~) + o_buf,
- * otherwise leave o for sketchssm_flush.  Never reads S. */
+ * otherwise leave o for sketchssm_flush.  Never reads S.  Mamba-2 layers
+ * need bufs->work (sketchssm_workspace_bytes). */
 int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                    const sketchssm_step* step, void* hip_stream);
 
@@ -154,6 +158,14 @@ int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* b
  * the W entries, write S, o = S^T q, count = 0.  Does not touch U. */
 int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                           const sketchssm_step* step, void* hip_stream);
+
+/* Bytes of the workspace bufs->work that sketchssm_read needs for this layer
+ * (0 when it needs none), or a negative SKSSM_E* code for an invalid layer.
+ * Mamba-2 uses it for the query's coordinates in every head's sketch basis,
+ * C_h q (B x R fp32), formed once per step for all heads of a B/C group
+ * (the decay factor of the pulled-back query is applied afterwards).  The
+ * caller allocates it; the library never does. */
+int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int sketchssm_version(void);

@@ -22,7 +22,7 @@ SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0
 SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP = 1, 2
 
 ENTRY_POINTS = ("sketchssm_read", "sketchssm_flush", "sketchssm_full_step",
-                "sketchssm_replay_step", "sketchssm_version")
+                "sketchssm_replay_step", "sketchssm_workspace_bytes", "sketchssm_version")
 
 
 class sketchssm_layer(C.Structure):
@@ -36,7 +36,7 @@ class sketchssm_buffers(C.Structure):
     _fields_ = [("S", C.c_void_p), ("U", C.c_void_p), ("Pt", C.c_void_p), ("C", C.c_void_p),
                 ("rank_offsets", C.c_void_p), ("ring_k", C.c_void_p), ("ring_v", C.c_void_p),
                 ("ring_gate", C.c_void_p), ("ring_beta", C.c_void_p), ("count", C.c_void_p),
-                ("A", C.c_void_p), ("err", C.c_void_p)]
+                ("A", C.c_void_p), ("err", C.c_void_p), ("work", C.c_void_p)]
 
 
 class sketchssm_step(C.Structure):
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
             fn.restype = C.c_int
         lib.sketchssm_flush.argtypes = [L, Bf, St, C.c_int32, C.c_void_p]
         lib.sketchssm_flush.restype = C.c_int
+        lib.sketchssm_workspace_bytes.argtypes = [L]
+        lib.sketchssm_workspace_bytes.restype = C.c_int64
         lib.sketchssm_version.argtypes = []
         lib.sketchssm_version.restype = C.c_int
         _lib = lib
@@ -94,6 +96,10 @@ def sketchssm_full_step(layer, bufs, step, stream=None) -> int:
 def sketchssm_replay_step(layer, bufs, step, stream=None) -> int:
     return load().sketchssm_replay_step(_ref(layer, sketchssm_layer), _ref(bufs, sketchssm_buffers),
                                         _ref(step, sketchssm_step), stream)
+
+
+def sketchssm_workspace_bytes(layer) -> int:
+    return load().sketchssm_workspace_bytes(_ref(layer, sketchssm_layer))
 
 
 def sketchssm_version() -> int:

@@ -23,8 +23,15 @@ bool shape_supported(int dk, int dv) {
 
 // What a call needs from the buffers and the step.
 struct Needs {
-  bool S, U, Pt, C, ring, count, step_in, step_q, step_o;
+  bool S, U, Pt, C, ring, count, step_in, step_q, step_o, work;
 };
+
+// Workspace of a read: the Mamba-2 query coordinates cq [B][R] fp32.
+int64_t workspace_bytes(const sketchssm_layer* L) {
+  if (L->family != SKSSM_MAMBA2) return 0;
+  const int64_t n = (int64_t)L->batch * L->rank_offsets_host[L->heads] * 4;
+  return (n + 255) / 256 * 256;
+}
 
 int check_layer(const sketchssm_layer* L) {
   if (!L) return SKSSM_EINVAL;
@@ -67,6 +74,7 @@ int check_buffers(const sketchssm_layer* L, const sketchssm_buffers* B, const sk
   }
   if (nd.count && (!aligned16(B->count) || !aligned16(B->err))) return SKSSM_EINVAL;
   if (L->family == SKSSM_MAMBA2 && !aligned16(B->A)) return SKSSM_EINVAL;
+  if (nd.work && workspace_bytes(L) > 0 && !aligned16(B->work)) return SKSSM_EINVAL;
   if (nd.step_in || nd.step_q || nd.step_o) {
     if (!S) return SKSSM_EINVAL;
     if (nd.step_in) {
@@ -99,6 +107,7 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.count = B->count;
   p.A = B->A;
   p.err = B->err;
+  p.work = B->work;
   if (S) {
     p.q = S->q;
     p.k = S->k;
@@ -131,7 +140,7 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{false, true, false, true, true, true, true, true, true};
+    const Needs nd{false, true, false, true, true, true, true, true, true, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_READ, make_params(layer, bufs, step), hip_stream);
   } catch (...) {
@@ -146,7 +155,7 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
     if (rc) return rc;
     if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL) return SKSSM_EFLAG;
     const bool out = step != nullptr;
-    const Needs nd{true, true, true, false, true, true, false, out, out};
+    const Needs nd{true, true, true, false, true, true, false, out, out, false};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     sk::Params p = make_params(layer, bufs, step);
     p.flush_all = flags == SKSSM_FLUSH_ALL;
@@ -165,7 +174,7 @@ int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* b
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{true, false, false, false, false, false, true, true, true};
+    const Needs nd{true, false, false, false, false, false, true, true, true, false};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_FULL, make_params(layer, bufs, step), hip_stream);
   } catch (...) {
@@ -178,9 +187,19 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{true, false, false, false, true, true, true, true, true};
+    const Needs nd{true, false, false, false, true, true, true, true, true, false};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_REPLAY, make_params(layer, bufs, step), hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer) {
+  try {
+    const int rc = check_layer(layer);
+    if (rc) return rc;
+    return workspace_bytes(layer);
   } catch (...) {
     return SKSSM_ELAUNCH;
   }

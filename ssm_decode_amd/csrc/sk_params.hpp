@@ -26,6 +26,7 @@ struct Params {
   int32_t* count;
   const float* A;
   int32_t* err;
+  void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
   const void* q;
   const void* k;
   const void* v;

@@ -42,7 +42,8 @@ class DeviceStep:
 
 class DecodeLayer:
     """All persistent buffers of one layer: S, U, Pt, C, rank offsets, the
-    ring (k, v, gate, beta), the per-tile ring counts, A and the error word."""
+    ring (k, v, gate, beta), the per-tile ring counts, A, the error word and
+    the read's workspace."""
 
     def __init__(self, family: str, batch: int, heads: int, qk_groups: int, dk: int, dv: int,
                  window: int, act: str, sketch: str, rank_offsets: np.ndarray,
@@ -80,10 +81,14 @@ class DecodeLayer:
         self._layer = abi.sketchssm_layer(
             FAMILY[family], B, H, G, dk, dv, W, DTYPE[act], DTYPE[sketch],
             self.offsets_host.ctypes.data_as(C.POINTER(C.c_int32)))
+        nwork = abi.sketchssm_workspace_bytes(self._layer)
+        if nwork < 0:
+            raise ValueError(f"invalid layer description (code {nwork})")
+        self.work = z((nwork,), torch.uint8) if nwork else None
         self._bufs = abi.sketchssm_buffers(
             _ptr(self.S), _ptr(self.U), _ptr(self.Pt), _ptr(self.Cmap), _ptr(self.offsets),
             _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_gate), _ptr(self.ring_beta),
-            _ptr(self.count), _ptr(self.A), _ptr(self.err))
+            _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work))
 
     # -------------------------------------------------------------- structs
     @property

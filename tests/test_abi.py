@@ -24,7 +24,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^int\s+(sketchssm_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t)\s+(sketchssm_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -56,7 +56,7 @@ def _layer(offsets, family=abi.SKSSM_MAMBA2, batch=2, heads=4, groups=4, dk=16, 
 
 def _bufs(**over):
     f = dict(S=FAKE, U=FAKE, Pt=FAKE, C=FAKE, rank_offsets=FAKE, ring_k=FAKE, ring_v=FAKE,
-             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE)
+             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE)
     f.update(over)
     return abi.sketchssm_buffers(**f)
 
@@ -139,3 +139,27 @@ def test_null_and_misaligned_pointers(lib):
 def test_bad_flag(lib):
     assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 2) == abi.SKSSM_EFLAG
     assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, -1) == abi.SKSSM_EFLAG
+
+
+def test_workspace_bytes(lib):
+    # Mamba-2: one fp32 per (sequence, coefficient row), rounded up to 256 bytes
+    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 256
+    off = np.concatenate([[0], np.cumsum(np.full(128, 8))]).astype(np.int32)
+    L = _layer(off, batch=320, heads=128, groups=8, dk=128, dv=64, W=16)
+    assert abi.sketchssm_workspace_bytes(L) == 320 * 1024 * 4
+    for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
+        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == 0
+    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, W=0)) == abi.SKSSM_EDIM
+    assert abi.sketchssm_workspace_bytes(None) == abi.SKSSM_EINVAL
+
+
+def test_read_needs_its_workspace(lib):
+    L = _layer(OK_OFF)
+    assert abi.sketchssm_read(L, _bufs(work=None), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(work=FAKE + 4), _step()) == abi.SKSSM_EINVAL
+    # the other calls, and families with no workspace, do not look at it
+    assert abi.sketchssm_flush(_layer(OK_OFF, batch=0), _bufs(work=None), None,
+                               abi.SKSSM_FLUSH_ALL) == 0
+    Lg = _layer(OK_OFF, family=abi.SKSSM_GDN, batch=0)
+    assert abi.sketchssm_read(Lg, _bufs(work=None), _step()) == 0
+    assert abi.sketchssm_read(_layer(OK_OFF, batch=0), _bufs(work=None), _step()) == 0
