@@ -22,7 +22,8 @@
  *  - ReplaySSM: buffered writes, full-state read each step (paper Sec. 1-2,
  *    App. D).
  *
- * Per family (readings where the pages are silent are listed in the design doc):
+ * Per family (the Mamba-2 write term, the KDA operator order and the gate
+ * dtypes are readings taken where the pages leave the step open):
  *   Mamba-2: M = a I, a = exp(-dt * exp(A_h)), B = dt k v^T
  *   GDN:     M = alpha (I - beta k k^T),        B = beta k v^T
  *   KDA:     M = (I - beta k k^T) Diag(g),      B = beta k v^T
