@@ -171,13 +171,62 @@ __device__ __forceinline__ void tr_reduce(float (&a)[N], int lane) {
     const int mask = 1 << (LB + s);
     const bool up = (lane & mask) != 0;
     const int half = (N >> (NB - 1 - s)) / 2;
+    // bitwise blend: a conditional on the two elements is folded by the
+    // compiler into a dynamically indexed read of the array (a select chain)
+    const uint32_t m = up ? 0xffffffffu : 0u;
 #pragma unroll
     for (int e = 0; e < half; ++e) {
-      const float send = up ? a[e] : a[e + half];
-      const float keep = up ? a[e + half] : a[e];
+      const uint32_t lo = __float_as_uint(a[e]), hi = __float_as_uint(a[e + half]);
+      const float send = __uint_as_float((lo & m) | (hi & ~m));
+      const float keep = __uint_as_float((hi & m) | (lo & ~m));
       a[e] = keep + __shfl_xor(send, mask);
     }
   }
+}
+
+// ---------------------------------------------------------- DPP reductions
+// Data-parallel-primitive moves read a neighbour lane's register inside the
+// VALU instruction (no LDS permute, no address arithmetic).  Control codes
+// (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_shl:n = 0x100 + n, row_mirror = 0x140, row_half_mirror = 0x141,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143.  Lanes outside ROW_MASK, and
+// lanes whose source lies outside the row, receive OLD.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float x, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+
+// Sum over each row of 16 lanes; every lane of the row receives it.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x, 0.f);
+  x += dpp_f<0x4E>(x, 0.f);
+  x += dpp_f<0x141>(x, 0.f);
+  x += dpp_f<0x140>(x, 0.f);
+  return x;
+}
+
+// Product over each row of 16 lanes; every lane of the row receives it.
+__device__ __forceinline__ float row16_prod(float x) {
+  x *= dpp_f<0xB1>(x, 1.f);
+  x *= dpp_f<0x4E>(x, 1.f);
+  x *= dpp_f<0x141>(x, 1.f);
+  x *= dpp_f<0x140>(x, 1.f);
+  return x;
+}
+
+// Value of lane L (a compile-time or wave-uniform index) in every lane.
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Sum over the 64 lanes of the wave, wave-uniform: row sums, then rows 0+1
+// and 2+3 by row_bcast:15, all four by row_bcast:31, read from lane 63.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x += dpp_f<0x142, 0xA>(x, 0.f);
+  x += dpp_f<0x143, 0xC>(x, 0.f);
+  return lane_value(x, 63);
 }
 
 // Mamba-2 decay a = exp(-dt * exp(A)).

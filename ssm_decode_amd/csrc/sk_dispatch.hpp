@@ -32,8 +32,11 @@ static int launch_shape(int mode, const Params& p, hipStream_t st) {
         hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 16>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
       else
         hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 32>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
-    } else
-      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT>), dim3(p.B * p.H), dim3(64), 0, st, p);
+    } else if (p.W <= 16) {
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, 16>), dim3(p.B * p.H), dim3(64), 0, st, p);
+    } else {
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, 32>), dim3(p.B * p.H), dim3(64), 0, st, p);
+    }
   } else if (p.W <= 16) {
     if (int rc = launch_tile<FAM, DK, DV, AT, UT, 16>(mode, p, st)) return rc;
   } else {

@@ -122,9 +122,10 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
   constexpr int CPL = DV / LPH;                  // output columns per lane
   constexpr int SPL = WMAX >= LPH ? WMAX / LPH : 1;  // ring slots per lane in the decay scan
   static_assert(SEG >= 1 && CPL >= 1, "head dims too small for the lane split");
-  static_assert(LPH >= 16, "one cq row per thread needs 16 lanes per head");
+  static_assert(LPH == 16, "a head is one 16-lane DPP row (and one cq row per thread)");
   __shared__ float s_d[WMAX];                    // d_i = k_i . q
   __shared__ float s_c[M2R_MAXHPG * 16];         // cq rows of the group
+  __shared__ __align__(16) float s_e[M2R_MAXHPG * WMAX];  // w_i d_i per head
 
   const int tid = threadIdx.x;
   const int hh = tid >> LB;                      // head within the group
@@ -146,9 +147,11 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
   const int rows = p.off[h0 + HPG] - roff0;
   const float Ah = p.A[h];
   int bad = (n0g < 0 || n0g >= W) ? ERRBIT_COUNT : 0;
-  if (mine != n0g) bad |= ERRBIT_GROUP;
   const int n0 = (n0g < 0 || n0g >= W) ? 0 : n0g; // in range for every address below
   const int n = n0 + 1;
+  // keep the count and offset loads ahead of every other load: the addresses
+  // below depend on them and the memory counter retires loads in order
+  __builtin_amdgcn_sched_barrier(0);
 
   const AT* q = reinterpret_cast<const AT*>(p.q) + bg * DK;
   const AT* kin = reinterpret_cast<const AT*>(p.k) + bg * DK;
@@ -165,36 +168,48 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
 
   if (n < W) {
     // ---------------------------------------------- issue the loads
+    // (loads are unconditional, from clamped indices, and their values are
+    // selected where used: a load behind a branch with a default value
+    // makes the wave wait for it inside the branch)
     float qs[SEG];
     ldn<SEG>(q + s * SEG, qs);
-    const float cqv = (tid < rows) ? reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + roff0 + tid] : 0.f;
+    const float cqv = reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + roff0 + min(tid, rows - 1)];
     // key of the first ring slot this head takes for the dot products
-    VecN<AT, SEG> k0 = kcur;
-    if (hh < n0) k0 = ldraw<SEG>(ring_k + (size_t)hh * DK + s * SEG);
+    const VecN<AT, SEG> k0r = ldraw<SEG>(ring_k + (size_t)(hh < n0 ? hh : 0) * DK + s * SEG);
+    AT dtr[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int i = s * SPL + u;
+      dtr[u] = ring_dt[i < n0 ? i : 0];
+    }
+    // sketch rows and ring values of the earlier entries (HBM).  Every row
+    // slot is loaded, rows past the head's rank or the ring fill from the
+    // last valid row (an L1 hit, no extra HBM traffic), so the number of
+    // loads in flight is fixed and the waits below retire only the loads
+    // they need.
+    VecN<UT, CPL> us[16];
+    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) us[j] = ldraw<CPL>(Ur + (size_t)min(j, r - 1) * DV);
+    VecN<AT, CPL> vs[WMAX];
+    const AT* rv0 = ring_v + s * CPL;
+    const int ilast = n0 > 0 ? n0 - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < WMAX - 1; ++i) vs[i] = ldraw<CPL>(rv0 + (size_t)min(i, ilast) * DV);
+
     float dts[SPL];
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
       const int i = s * SPL + u;
-      dts[u] = (i < n0) ? ld(ring_dt + i) : (i == n0 ? to_f32(dtcur) : 0.f);
+      dts[u] = (i < n0) ? to_f32(dtr[u]) : (i == n0 ? to_f32(dtcur) : 0.f);
     }
-    // sketch rows and ring values of the earlier entries (HBM)
-    VecN<UT, CPL> us[16];
-    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < r) us[j] = ldraw<CPL>(Ur + (size_t)j * DV);
-    VecN<AT, CPL> vs[WMAX];
-    const AT* rv0 = ring_v + s * CPL;
-#pragma unroll
-    for (int i = 0; i < WMAX - 1; ++i)
-      if (i < n0) vs[i] = ldraw<CPL>(rv0 + (size_t)i * DV);
-
     // d_i = k_i . q, slots spread over the group's heads (LPH lanes per slot)
     if (hh < n) {
+      const VecN<AT, SEG> k0 = hh < n0 ? k0r : kcur;
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < SEG; ++e) d += vget(k0, e) * qs[e];
-      d = xsum<0, LB>(d);
+      d = row16_sum(d);
       if (s == 0) s_d[hh] = d;
     }
     for (int i = hh + HPG; i < n; i += HPG) {
@@ -208,7 +223,7 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < SEG; ++e) d += ks[e] * qs[e];
-      d = xsum<0, LB>(d);
+      d = row16_sum(d);
       if (s == 0) s_d[i] = d;
     }
     if (tid < rows) s_c[tid] = cqv;
@@ -221,16 +236,15 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
       a[u] = (i < n) ? m2_decay(dts[u], Ah) : 1.0f;
       lp *= a[u];
     }
+    // suffix products along the head's DPP row (row_shl:n reads lane s+n;
+    // lanes past the row end read 1)
     float incl = lp;                               // prod over lanes >= s
-#pragma unroll
-    for (int d = 1; d < LPH; d <<= 1) {
-      const float o = __shfl_down(incl, d, LPH);
-      if (s + d < LPH) incl *= o;
-    }
-    // shuffle with every lane active (a disabled source lane reads as zero)
-    const float nxt = __shfl_down(incl, 1, LPH);
-    const float after = (s + 1 < LPH) ? nxt : 1.0f;   // prod over lanes > s
-    const float D = __shfl(incl, 0, LPH);
+    incl *= dpp_f<0x101>(incl, 1.f);
+    incl *= dpp_f<0x102>(incl, 1.f);
+    incl *= dpp_f<0x104>(incl, 1.f);
+    incl *= dpp_f<0x108>(incl, 1.f);
+    const float after = dpp_f<0x101>(incl, 1.f); // prod over lanes > s
+    const float D = row16_prod(lp);
     float w[SPL];
     {
       float suf = after;
@@ -240,15 +254,18 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
         suf *= a[u];
       }
     }
+    if (mine != n0g) bad |= ERRBIT_GROUP;
     if (__syncthreads_or(bad)) {                   // s_d and s_c complete
       if (s == 0 && bad) atomicOr(p.err, bad);
       return;
     }
-    float e[SPL];
+    // e_i = w_i d_i, exchanged within the head's row through LDS (a wave
+    // reads back what its own lanes wrote: LDS keeps a wave's order)
+    float* eh = s_e + hh * WMAX;
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
       const int i = s * SPL + u;
-      e[u] = (i < n) ? w[u] * s_d[i] : 0.f;
+      eh[i] = (i < n) ? w[u] * s_d[i] : 0.f;
     }
 
     // ------------------------------------------------------- output
@@ -266,17 +283,13 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
     }
 #pragma unroll
     for (int i = 0; i < WMAX - 1; ++i) {
-      const float ei = __shfl(e[i % SPL], i / SPL, LPH);
+      const float ei = eh[i];
       if (i < n0)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) ob[c] += ei * vget(vs[i], c);
     }
     {
-      float ecur = e[0];
-#pragma unroll
-      for (int u = 1; u < SPL; ++u)
-        if (n0 % SPL == u) ecur = e[u];
-      ecur = __shfl(ecur, n0 / SPL, LPH);
+      const float ecur = eh[n0];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) ob[c] += ecur * vget(vcur, c);
     }
@@ -284,9 +297,12 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
 #pragma unroll
     for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
     stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
-  } else if (__syncthreads_or(bad)) {              // pairs with the barrier above
-    if (s == 0 && bad) atomicOr(p.err, bad);
-    return;
+  } else {
+    if (mine != n0g) bad |= ERRBIT_GROUP;
+    if (__syncthreads_or(bad)) {                   // pairs with the barrier above
+      if (s == 0 && bad) atomicOr(p.err, bad);
+      return;
+    }
   }
 
   // ------------------------------------------------------------ append
@@ -301,132 +317,154 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
 }
 
 // ------------------------------------------------------------ GDN / KDA
-// One wave per (sequence, head) tile.  The pull-back is a serial chain over
-// the buffered entries, newest first:
+// One wave per (sequence, head) tile.  Every load is issued once the ring
+// fill is known, before any arithmetic: the step's own entry, the buffered
+// entries (keys, values, gates, betas), the coefficient rows of C (L2
+// resident) and the sketch rows of U.  The pull-back is then a chain over
+// the buffered entries held in registers, newest first:
 //   d = k_i . r;  o_buf += beta_i d v_i;  r <- alpha_i (r - beta_i d k_i)   (GDN)
 //                                        r <- g_i (.) (r - beta_i d k_i)    (KDA)
-// then c = C_h r and o = U_h c + o_buf.  Each lane holds DK/64 elements of r
-// and DV/64 output columns.
-template <int FAM, int DK, int DV, typename AT, typename UT>
+// then c = C_h r and o = U_h c + o_buf.  Lane l holds the key elements
+// EK l .. EK l + EK - 1 of r and k_i and the output columns EV l .. ; the
+// per-slot scalars of slot i sit in lane i and are read with readlane.  The
+// append stores the step's entry from the registers that hold it.
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
 __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
   constexpr int EK = DK >= 64 ? DK / 64 : 1;
   constexpr int EV = DV >= 64 ? DV / 64 : 1;
+  constexpr int KG = FAM == FAM_KDA ? EK : 1;    // gate elements per lane and slot
   const int lane = threadIdx.x;
   const int W = p.W;
   const int tile = blockIdx.x;
   const int b = tile / p.H;
   const int h = tile - b * p.H;
   const size_t bh = (size_t)b * p.H + h;      // G == H for these families
+  const bool kl = lane * EK < DK;             // lane holds key elements
+  const bool vl = lane * EV < DV;             // lane holds output columns
+  // lanes without elements (small heads) load a valid element and drop it,
+  // so no load sits behind a per-lane branch
+  const int lk = kl ? lane * EK : 0;
+  const int lv = vl ? lane * EV : 0;
 
+  // the ring fill and the rank offsets first: every address below depends
+  // on them, and the memory counter retires loads in order
   const int n0 = p.count[bh];
+  const int off = p.off[h], rk = p.off[h + 1] - off;
   if (n0 < 0 || n0 >= W) {
     if (lane == 0) atomicOr(p.err, ERRBIT_COUNT);
     return;
   }
   const int n = n0 + 1;
-  const AT* kin = reinterpret_cast<const AT*>(p.k) + bh * DK;
-  const AT* vin = reinterpret_cast<const AT*>(p.v) + bh * DV;
-  const float* gin = reinterpret_cast<const float*>(p.gate) + (FAM == FAM_KDA ? bh * DK : bh);
-  AT* ring_k = reinterpret_cast<AT*>(p.rk) + bh * W * DK;
-  AT* ring_v = reinterpret_cast<AT*>(p.rv) + bh * W * DV;
-  float* ring_g = reinterpret_cast<float*>(p.rg) + (FAM == FAM_KDA ? bh * W * DK : bh * W);
+  __builtin_amdgcn_sched_barrier(0);
+  const AT* kin = reinterpret_cast<const AT*>(p.k) + bh * DK + lk;
+  const AT* vin = reinterpret_cast<const AT*>(p.v) + bh * DV + lv;
+  const float* gin = reinterpret_cast<const float*>(p.gate) + (FAM == FAM_KDA ? bh * DK + lk : bh);
+  AT* ring_k = reinterpret_cast<AT*>(p.rk) + bh * W * DK + lk;
+  AT* ring_v = reinterpret_cast<AT*>(p.rv) + bh * W * DV + lv;
+  float* ring_g = reinterpret_cast<float*>(p.rg) + (FAM == FAM_KDA ? bh * W * DK + lk : bh * W);
   float* ring_b = p.rb + bh * W;
 
-  // append
-  for (int e = lane; e < DK; e += 64) ring_k[(size_t)n0 * DK + e] = kin[e];
-  for (int e = lane; e < DV; e += 64) ring_v[(size_t)n0 * DV + e] = vin[e];
+  // ------------------------------------------ the step's own entry
+  const VecN<AT, EK> kcur = ldraw<EK>(kin);
+  const VecN<AT, EV> vcur = ldraw<EV>(vin);
+  float gcur[KG];
+  if (FAM == FAM_KDA) ldn<KG>(gin, gcur);
+  else gcur[0] = gin[0];
+  const float bcur = p.beta[bh];
+
+  if (n < W) {
+    // ------------------------------------------------ issue the loads
+    float r[EK];
+    ldn<EK>(reinterpret_cast<const AT*>(p.q) + bh * DK + lk, r);
+    if (!kl)
+#pragma unroll
+      for (int e = 0; e < EK; ++e) r[e] = 0.f;
+    VecN<AT, EK> ks[WMAX - 1];
+    VecN<AT, EV> vs[WMAX - 1];
+    float gs[WMAX - 1][KG];
+#pragma unroll
+    for (int i = 0; i < WMAX - 1; ++i) {
+      if (i < n0) {                                // uniform
+        ks[i] = ldraw<EK>(ring_k + (size_t)i * DK);
+        vs[i] = ldraw<EV>(ring_v + (size_t)i * DV);
+        if (FAM == FAM_KDA) ldn<KG>(ring_g + (size_t)i * DK, gs[i]);
+      }
+    }
+    // GDN / KDA per-slot scalars: slot i in lane i
+    const int ls = lane < n0 ? lane : 0;
+    const float al_l = FAM == FAM_GDN ? ring_g[ls] : 1.f;
+    const float be_l = ring_b[ls];
+    float cr[16][EK];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < rk) ldn<EK>(p.C + (size_t)(off + j) * DK + lk, cr[j]);
+    VecN<UT, EV> us[16];
+    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + lv;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < rk) us[j] = ldraw<EV>(Ur + (size_t)j * DV);
+
+    // ---------------------------------------- pull-back, newest first
+    float ob[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) ob[e] = 0.f;
+    auto entry = [&](const VecN<AT, EK>& kv, const VecN<AT, EV>& vv, const float* gv, float be) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) d += vget(kv, e) * r[e];   // r is 0 where !kl
+      d = wave_sum(d);
+      const float bd = be * d;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) ob[e] += bd * vget(vv, e);
+#pragma unroll
+      for (int e = 0; e < EK; ++e) {
+        const float dec = FAM == FAM_GDN ? gv[0] : gv[e];
+        r[e] = kl ? dec * (r[e] - bd * vget(kv, e)) : 0.f;
+      }
+    };
+    entry(kcur, vcur, gcur, bcur);
+#pragma unroll
+    for (int i = WMAX - 2; i >= 0; --i) {
+      if (i < n0) {
+        float gsc[KG];
+        if (FAM == FAM_GDN) gsc[0] = lane_value(al_l, i);
+        else
+#pragma unroll
+          for (int e = 0; e < KG; ++e) gsc[e] = gs[i][e];
+        entry(ks[i], vs[i], gsc, lane_value(be_l, i));
+      }
+    }
+
+    // -------------------------- c = C_h r, then o = U_h c + o_buf
+    // (each c_j is a wave sum, wave-uniform, so U_h c needs no broadcast)
+    float out[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) out[e] = ob[e];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < rk) {                                // uniform
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EK; ++e) a += cr[j][e] * r[e];
+        const float cj = wave_sum(a);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) out[e] += cj * vget(us[j], e);
+      }
+    }
+    if (vl) stn<EV>(reinterpret_cast<AT*>(p.o) + bh * DV + lv, out);
+  }
+
+  // ------------------------------------------------------------ append
+  if (kl) stv<EK>(ring_k + (size_t)n0 * DK, kcur);
+  if (vl) stv<EV>(ring_v + (size_t)n0 * DV, vcur);
   if (FAM == FAM_KDA) {
-    for (int e = lane; e < DK; e += 64) ring_g[(size_t)n0 * DK + e] = gin[e];
+    if (kl) stn<KG>(ring_g + (size_t)n0 * DK, gcur);
   } else if (lane == 0) {
-    ring_g[n0] = gin[0];
+    ring_g[n0] = gcur[0];
   }
   if (lane == 0) {
-    ring_b[n0] = p.beta[bh];
+    ring_b[n0] = bcur;
     p.count[bh] = n;
-  }
-  if (n == W) return;
-
-  float r[EK], ob[EV];
-  const AT* q = reinterpret_cast<const AT*>(p.q) + bh * DK;
-#pragma unroll
-  for (int e = 0; e < EK; ++e) {
-    const int m = lane * EK + e;
-    r[e] = (m < DK) ? ld(q + m) : 0.f;
-  }
-#pragma unroll
-  for (int e = 0; e < EV; ++e) ob[e] = 0.f;
-
-  for (int t = 0; t < n; ++t) {
-    const int i = n - 1 - t;
-    const AT* k = (i == n0) ? kin : ring_k + (size_t)i * DK;
-    const AT* v = (i == n0) ? vin : ring_v + (size_t)i * DV;
-    const float beta = (i == n0) ? p.beta[bh] : ring_b[i];
-    float kk[EK];
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-      const int m = lane * EK + e;
-      kk[e] = (m < DK) ? ld(k + m) : 0.f;
-      d += kk[e] * r[e];
-    }
-    d = xsum<0, 6>(d);
-    const float bd = beta * d;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) {
-      const int c = lane * EV + e;
-      if (c < DV) ob[e] += bd * ld(v + c);
-    }
-    if (FAM == FAM_GDN) {
-      const float al = (i == n0) ? gin[0] : ring_g[i];
-#pragma unroll
-      for (int e = 0; e < EK; ++e) r[e] = al * (r[e] - bd * kk[e]);
-    } else {
-      const float* gv = (i == n0) ? gin : ring_g + (size_t)i * DK;
-#pragma unroll
-      for (int e = 0; e < EK; ++e) {
-        const int m = lane * EK + e;
-        const float gm = (m < DK) ? gv[m] : 0.f;
-        r[e] = gm * (r[e] - bd * kk[e]);
-      }
-    }
-  }
-
-  // c = C_h r : 16 partial dot products, halved across lane bits 2..5, summed over bits 0..1
-  const int off = p.off[h], rk = p.off[h + 1] - off;
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float a = 0.f;
-    if (j < rk) {
-      const float* Cr = p.C + (size_t)(off + j) * DK;
-#pragma unroll
-      for (int e = 0; e < EK; ++e) {
-        const int m = lane * EK + e;
-        if (m < DK) a += Cr[m] * r[e];
-      }
-    }
-    acc[j] = a;
-  }
-  tr_reduce<16, 2, 4>(acc, lane);
-  const float cj_mine = xsum<0, 2>(acc[0]);      // c_j for j = lane >> 2
-
-  const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV;
-  float out[EV];
-#pragma unroll
-  for (int e = 0; e < EV; ++e) out[e] = ob[e];
-  for (int j = 0; j < rk; ++j) {
-    const float cj = __shfl(cj_mine, 4 * j);
-#pragma unroll
-    for (int e = 0; e < EV; ++e) {
-      const int c = lane * EV + e;
-      if (c < DV) out[e] += cj * ld(Ur + (size_t)j * DV + c);
-    }
-  }
-  AT* o = reinterpret_cast<AT*>(p.o) + bh * DV;
-#pragma unroll
-  for (int e = 0; e < EV; ++e) {
-    const int c = lane * EV + e;
-    if (c < DV) st(o + c, out[e]);
   }
 }
 

@@ -4,8 +4,11 @@
 // kernel: it is loaded once with 128-bit loads, updated, reduced against the
 // query / basis vectors and stored once.
 //
-// Register layout.  The dv columns are split into column blocks of CB = 64
-// (or dv when smaller), one wave per block.  With cg = lane % 16 and
+// Register layout.  The dv columns are split into column blocks of CB
+// columns, one wave per block: 64 for dv = 64 (one wave holds a 128 x 64
+// tile in 128 registers per lane), 32 for dv = 128 (four waves of 64
+// registers each, which keeps the delta-rule kernels free of spills), dv
+// when smaller.  With cg = lane % 16 and
 // rg = lane / 16, lane l holds the NCC = CB/16 consecutive columns
 // NCC*cg .. NCC*cg+NCC-1 of its block and, for every 16-row block mb, the four
 // consecutive rows 16*mb + 4*rg + v (v = 0..3):
@@ -38,7 +41,7 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV>
 struct TileShape {
-  static constexpr int CB = DV >= 64 ? 64 : DV;   // columns per wave
+  static constexpr int CB = DV >= 128 ? 32 : (DV >= 64 ? 64 : DV);   // columns per wave
   static constexpr int NCB = DV / CB;             // waves per tile
   static constexpr int NCC = CB / 16;             // consecutive columns per lane
   static constexpr int MB = DK / 16;              // 16-row blocks
