@@ -1,14 +1,13 @@
 // Tile kernels: one workgroup per (sequence, head) tile that reads the full
 // state.  Used by the flush, the standard full-state step and the ReplaySSM
 // step.  The state tile S (dk x dv fp32) is held in registers for the whole
-// kernel: it is loaded once with 128-bit loads, updated, reduced against the
+// kernel: it is loaded once with wide loads, updated, reduced against the
 // query / basis vectors and stored once.
 //
-// Register layout.  The dv columns are split into column blocks of CB
-// columns, one wave per block: 64 for dv = 64 (one wave holds a 128 x 64
-// tile in 128 registers per lane), 32 for dv = 128 (four waves of 64
-// registers each, which keeps the delta-rule kernels free of spills), dv
-// when smaller.  With cg = lane % 16 and
+// Register layout.  The dv columns are split into column blocks of CB = 32
+// columns (dv when smaller), one wave per block: a 128 x 32 block is 64
+// registers per lane, which leaves room for the delta-rule and ReplaySSM
+// paths without spills and runs 3-4 waves per SIMD.  With cg = lane % 16 and
 // rg = lane / 16, lane l holds the NCC = CB/16 consecutive columns
 // NCC*cg .. NCC*cg+NCC-1 of its block and, for every 16-row block mb, the four
 // consecutive rows 16*mb + 4*rg + v (v = 0..3):
@@ -20,7 +19,8 @@
 //   - the A-operand layout (A[cg][rg]) of the same instruction for S^T, with
 //     K-step (mb, v) covering rows 16 mb + 4 k + v, so U = S^T P needs no
 //     data movement either;
-// and every lane's four columns of a row are one 128-bit load or store.
+// and every lane's NCC columns of a row are one 64-bit (NCC = 2) or 128-bit
+// (NCC = 4) load or store.
 //
 // Latency structure.  Every global load the tile needs besides the state
 // (ring keys, values and gates, the basis rows, the query) is issued first,
@@ -41,7 +41,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV>
 struct TileShape {
-  static constexpr int CB = DV >= 128 ? 32 : (DV >= 64 ? 64 : DV);   // columns per wave
+  // columns per wave: 32 (a 128 x 32 block is 64 registers per lane), or dv
+  // when smaller
+  static constexpr int CB = DV >= 64 ? 32 : DV;
   static constexpr int NCB = DV / CB;             // waves per tile
   static constexpr int NCC = CB / 16;             // consecutive columns per lane
   static constexpr int MB = DK / 16;              // 16-row blocks
@@ -457,11 +459,26 @@ tile_kernel(Params p) {
   } else {
     // ----------------------- ReplaySSM non-flush: exact S0^T q~ + o_buf
     if (FAM == FAM_M2) {
-      // q~ = D q ; buffered term sum_i (k_i . q) (w_i v_i)
-      if (wv == 0 && lane < n) {
-        float d = 0.f;
-        for (int m = 0; m < DK; ++m) d += s_k[m * KWS + lane] * s_q[m];
-        s_e[lane] = d;
+      // q~ = D q ; buffered term sum_i (k_i . q) (w_i v_i): wave 0 forms the
+      // n dot products as DPP wave sums over the key elements
+      if (wv == 0) {
+        constexpr int EK = DK >= 64 ? DK / 64 : 1;
+        float qq[EK];
+#pragma unroll
+        for (int e = 0; e < EK; ++e) {
+          const int m = lane * EK + e;
+          qq[e] = m < DK ? s_q[m] : 0.f;
+        }
+        for (int i = 0; i < n; ++i) {            // uniform
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < EK; ++e) {
+            const int m = lane * EK + e;
+            if (m < DK) d += s_k[m * KWS + i] * qq[e];
+          }
+          d = wave_sum(d);
+          if (lane == 0) s_e[i] = d;
+        }
       }
       const float D = s_misc[0];
       for (int m = tid; m < DK; m += NT) s_qt[m] = D * s_q[m];
@@ -485,7 +502,7 @@ tile_kernel(Params p) {
           kk[e] = (m < DK) ? s_k[i * DK + m] : 0.f;
           d += kk[e] * r[e];
         }
-        d = xsum<0, 6>(d);
+        d = wave_sum(d);
         const float beta = s_w[i];
         if (lane == 0) s_e[i] = beta * d;
 #pragma unroll
