@@ -9,17 +9,16 @@ namespace sk {
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
 static int launch_tile(int mode, const Params& p, hipStream_t st) {
-  const size_t lds = TileLds<FAM, DK, DV, WMAX>::BYTES;
-  const dim3 grid(p.B * p.H);
+  const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
+  constexpr size_t lds_flush = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH>::BYTES;
+  constexpr size_t lds_full = TileLds<FAM, DK, DV, WMAX, MODE_FULL>::BYTES;
+  constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY>::BYTES;
   if (mode == MODE_FLUSH)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX>), grid,
-                       dim3(TileShape<DK, DV>::THREADS), lds, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX>), grid, block, lds_flush, st, p);
   else if (mode == MODE_FULL)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX>), grid,
-                       dim3(TileShape<DK, DV>::THREADS), lds, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX>), grid, block, lds_full, st, p);
   else if (mode == MODE_REPLAY)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX>), grid,
-                       dim3(TileShape<DK, DV>::THREADS), lds, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX>), grid, block, lds_replay, st, p);
   else
     return -4;
   return 0;

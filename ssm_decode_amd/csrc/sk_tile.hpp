@@ -54,7 +54,7 @@ struct TileShape {
 };
 
 // LDS layout of a tile kernel (offsets in floats).
-template <int FAM, int DK, int DV, int WMAX>
+template <int FAM, int DK, int DV, int WMAX, int MODE>
 struct TileLds {
   using T = TileShape<DK, DV>;
   static constexpr int KWS = WMAX + 4;                         // Mamba-2 key row stride ([m][slot])
@@ -70,9 +70,20 @@ struct TileLds {
   static constexpr int KEYS = FAM == FAM_M2 ? DK * KWS : WMAX * DK * (FAM == FAM_KDA ? 2 : 1);
   static constexpr int BASIS = DK * T::PS;                     // basis [m][j], over the keys after the update
   static constexpr int P0 = KEYS0;
-  static constexpr int TOTAL = KEYS0 + (KEYS > BASIS ? KEYS : BASIS);
+  // GDN/KDA chunked update, after the raw keys (and KDA gates):
+  static constexpr int KQ = KEYS0 + KEYS;                      // k_i (.) Gamma_i   [m][slot]
+  static constexpr int KD = KQ + DK * KWS;                     // k_i (/) Gamma_i   [m][slot]
+  static constexpr int AM = KD + DK * KWS;                     // A [i][j], stride WMAX + 1
+  static constexpr int GF = AM + round4(WMAX * (WMAX + 1));    // Gamma after the last entry [dk]
+  // (only the flush reserves them: the ReplaySSM step flushes one step in W
+  // and takes the serial form, keeping its LDS and occupancy)
+  static constexpr bool CHUNK = FAM != FAM_M2 && MODE == MODE_FLUSH;
+  static constexpr int DN_END = CHUNK ? GF + DK : 0;
+  static constexpr int T0 = KEYS0 + (KEYS > BASIS ? KEYS : BASIS);
+  static constexpr int TOTAL = T0 > DN_END ? T0 : DN_END;
   static constexpr int BYTES = TOTAL * 4;
-  static_assert(V % 4 == 0 && KEYS0 % 4 == 0 && P0 % 4 == 0, "LDS regions must be 16-byte aligned");
+  static_assert(V % 4 == 0 && KEYS0 % 4 == 0 && P0 % 4 == 0 && GF % 4 == 0,
+                "LDS regions must be 16-byte aligned");
 };
 
 template <typename AT>
@@ -97,11 +108,13 @@ __device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, d, 0, 0, 0);
 }
 
+// (the delta-rule flush runs three waves per SIMD: its chunked update has
+// serial phases that more resident tiles hide)
 template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX>
-__global__ void __launch_bounds__((TileShape<DK, DV>::THREADS), 2)
+__global__ void __launch_bounds__((TileShape<DK, DV>::THREADS), (MODE == MODE_FLUSH && FAM != FAM_M2 ? 3 : 2))
 tile_kernel(Params p) {
   using T = TileShape<DK, DV>;
-  using LY = TileLds<FAM, DK, DV, WMAX>;
+  using LY = TileLds<FAM, DK, DV, WMAX, MODE>;
   constexpr int CB = T::CB, NCC = T::NCC, MB = T::MB, PS = T::PS;
   constexpr int NT = T::THREADS;
   constexpr int KWS = LY::KWS;
@@ -379,8 +392,141 @@ tile_kernel(Params p) {
         }
       }
     } else {
-      // delta rule, one entry at a time
-      for (int i = 0; i < n; ++i) {
+      // Delta rule.  With Gamma_i = g_1 (.) .. (.) g_i (GDN: alpha_1 .. alpha_i
+      // on every channel), kq_i = k_i (.) Gamma_i and kd_j = k_j (/) Gamma_j,
+      // the n updates S_i = (I - b_i k_i k_i^T) Diag(g_i) S_{i-1} + b_i k_i v_i^T
+      // are, with e_i = b_i (v_i - (Diag(g_i) S_{i-1})^T k_i),
+      //   (I + A) E = diag(b) (V - Kq S0),   A_ij = b_i kq_i . kd_j  (j < i)
+      //   S_n = Diag(Gamma_n) (S0 + Kd^T E)
+      // (the unrolled recurrence; a WY-style chunk).  Kq S0 and Kd^T E run on
+      // the matrix cores in the state's register layout; the n x n system is
+      // solved by forward substitution, one column per thread.  Tiles whose
+      // Gamma underflows (tiny gates) and single entries take the serial
+      // path below.
+      float* s_kq = smem + LY::KQ;
+      float* s_kd = smem + LY::KD;
+      float* s_A = smem + LY::AM;
+      float* s_gf = smem + LY::GF;
+      constexpr int AS = WMAX + 1;
+      bool chunked = false;
+      if (LY::CHUNK && n >= 4) {                     // uniform
+        int small = 0;
+        for (int m = tid; m < DK; m += NT) {
+          float G = 1.f;
+          for (int i = 0; i < WMAX; ++i) {
+            float kq = 0.f, kd = 0.f;
+            if (i < n) {
+              G *= (FAM == FAM_GDN) ? s_a[i] : s_k[(WMAX + i) * DK + m];
+              const float k = s_k[i * DK + m];
+              kq = k * G;
+              kd = k / G;
+            }
+            s_kq[m * KWS + i] = kq;
+            s_kd[m * KWS + i] = kd;
+          }
+          s_gf[m] = G;
+          small |= !(G >= 1e-30f) ? 1 : 0;         // also catches NaN
+        }
+        chunked = !__syncthreads_or(small);
+      }
+      if (chunked) {
+        constexpr int NE = cdiv(WMAX, 16);           // 16-entry blocks
+        // X^T = S0^T Kq^T: lane (cg, rg) gets X[16 t + cg][NCC (4 rg + vv) + c]
+        f32x4v xacc[NE][NCC];
+#pragma unroll
+        for (int t = 0; t < NE; ++t)
+#pragma unroll
+          for (int c = 0; c < NCC; ++c) xacc[t][c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NE; ++t) {
+          if (16 * t < n) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float bq = s_kq[(16 * mb + 4 * rg + v) * KWS + 16 * t + cg];
+#pragma unroll
+                for (int c = 0; c < NCC; ++c) xacc[t][c] = mfma16x4(sacc[mb][c][v], bq, xacc[t][c]);
+              }
+          }
+        }
+        // A (wave 0): D[i][j] = kq_i . kd_j over 16 x 16 blocks, lower part kept
+        if (wv == 0) {
+#pragma unroll
+          for (int it = 0; it < NE; ++it)
+#pragma unroll
+            for (int jt = 0; jt <= it; ++jt) {
+              if (16 * it < n) {
+                f32x4v a = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+                for (int ks = 0; ks < DK / 4; ++ks)
+                  a = mfma16x4(s_kq[(4 * ks + rg) * KWS + 16 * it + cg],
+                               s_kd[(4 * ks + rg) * KWS + 16 * jt + cg], a);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const int i = 16 * it + 4 * rg + v, j = 16 * jt + cg;
+                  s_A[i * AS + j] = (j < i && i < n) ? s_w[i] * a[v] : 0.f;
+                }
+              }
+            }
+        }
+        // R = diag(b) (V - X), in place over the values
+#pragma unroll
+        for (int t = 0; t < NE; ++t) {
+          const int i = 16 * t + cg;
+          if (i < n) {
+            const float be = s_w[i];
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+              for (int c = 0; c < NCC; ++c) {
+                float* x = s_v + i * DV + wv * CB + NCC * (4 * rg + vv) + c;
+                *x = be * (*x - xacc[t][c][vv]);
+              }
+          }
+        }
+        __syncthreads();
+        // forward substitution, one column per thread: E overwrites R; the
+        // padding rows up to a multiple of four become zero
+        if (tid < DV) {
+          float e[WMAX];
+#pragma unroll
+          for (int i = 0; i < WMAX; ++i) {
+            if (i < n) {
+              float x = s_v[i * DV + tid];
+#pragma unroll
+              for (int j = 0; j < i; ++j) x -= s_A[i * AS + j] * e[j];
+              e[i] = x;
+              s_v[i * DV + tid] = x;
+            } else if (i < round4(n)) {
+              s_v[i * DV + tid] = 0.f;
+            }
+          }
+        }
+        __syncthreads();
+        // S0 + Kd^T E on the matrix cores, then the row scaling Diag(Gamma_n)
+        for (int t4 = 0; t4 < n; t4 += 4) {
+          float bv[NCC];
+          ldn<NCC>(s_v + (t4 + rg) * DV + colbase, bv);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const float ak = s_kd[(16 * mb + cg) * KWS + t4 + rg];
+#pragma unroll
+            for (int c = 0; c < NCC; ++c) sacc[mb][c] = mfma16x4(ak, bv[c], sacc[mb][c]);
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const float4 g4 = *reinterpret_cast<const float4*>(s_gf + 16 * mb + 4 * rg);
+          const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int c = 0; c < NCC; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sacc[mb][c][v] *= gv[v];
+        }
+      }
+      // serial form: one entry at a time
+      for (int i = 0; !chunked && i < n; ++i) {
         float kk[MB][4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
