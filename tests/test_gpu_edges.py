@@ -170,3 +170,52 @@ def test_group_count_mismatch_sets_error():
     assert cnt[0, 0] == 0 and cnt[0, 1] == 1           # group 0 of sequence 0 untouched
     assert (cnt[0, 2:] == 1).all() and (cnt[1] == 1).all()
     assert (step.o[0, :2].float().cpu().numpy() == 3.0).all()
+
+
+@pytest.mark.parametrize("family,power,seed", [("gdn", 160, 37), ("kda", 60, 38), ("kda", 4, 39)])
+def test_small_gates(family, power, seed):
+    """Gates raised to a power (the same values on both sides): with tiny
+    gates the product of a window's gates underflows on some tiles, which
+    then take the serial form of the flush; the others the chunked form.
+    Outputs and states against the oracle over three windows."""
+    import dataclasses
+    import synth
+    import oracle
+    from ssm_decode_amd import abi, feed
+    from ssm_decode_amd.feed import to_device
+    from tests.gpu_parity import rel_l2, all_tiles
+    cfg = _tiny(family, seed, name=f"gates_{family}_{power}", window=8, batch=3, heads=4,
+                qk_groups=4)
+    li = synth.make_layer_inputs(cfg)
+    tiles = all_tiles(cfg)
+    lay = feed.make_layer(cfg, li)
+    feed.fill_state(lay, cfg, numpy_all=True)
+    assert feed.prime(lay, li) == 0
+    S0 = synth.initial_state(cfg).reshape(-1, cfg.dk, cfg.dv)
+    orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, cfg.window, li.ranks, li.offsets, li.Pt,
+                             li.C, li.A, tiles, S0, cfg.heads, cfg.qk_groups)
+    assert orc.flush(None, all_tiles=True)[0] == 0
+    step = lay.new_step()
+    worst_o = worst_s = 0.0
+    for t in range(3 * cfg.window):
+        si = synth.make_step_inputs(cfg, t)
+        si = dataclasses.replace(si, gate=synth.round_f32(si.gate ** power))
+        feed.fill_step(step, cfg, t, numpy_all=True)
+        step.gate.copy_(to_device(si.gate, "f32", step.gate.device))
+        assert lay.read(step) == 0 and lay.flush(step, abi.SKSSM_FLUSH_DUE) == 0
+        o = np.zeros((len(tiles), cfg.dv))
+        assert orc.read(si, o=o)[0] == 0
+        due = orc.count == cfg.window
+        if due.any():
+            assert orc.flush(si, o=o)[0] == 0
+        torch.cuda.synchronize()
+        e = rel_l2(step.o.cpu().numpy().reshape(-1, cfg.dv), o)
+        worst_o = max(worst_o, e)
+        assert e <= 1e-5, (t, e)
+        if due.any():
+            S_gpu = lay.S.cpu().numpy().reshape(-1, cfg.dk, cfg.dv).astype(np.float64)
+            es = rel_l2(S_gpu, orc.S)
+            worst_s = max(worst_s, es)
+            assert es <= 1e-5, (t, es)
+    assert lay.error_word() == 0
+    print(f"  gates^{power}: max rel-L2 o={worst_o:.2e} S={worst_s:.2e}")
