@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-baselines", action="store_true", help="skip full/replay GPU baselines")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
-    ap.add_argument("--cpu-windows", type=int, default=12, help="windows in the CPU sample")
+    ap.add_argument("--cpu-windows", type=int, default=16, help="windows in the CPU sample")
     return ap.parse_args()
 
 
@@ -240,6 +240,12 @@ def main():
         }
         log(f"[bench] baselines: {baselines}")
 
+    # ------------------------- sketch approximation error (information only)
+    approx = None
+    if not args.no_baselines:
+        approx = sketch_error(cfg, li, layers[0], pool, steps=2 * W)
+        log(f"[bench] sketched vs exact read: {approx}")
+
     # ------------------------------------------ copy-bandwidth reference
     nbytes = 2 * 2 ** 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -304,6 +310,7 @@ def main():
                             "copy-calibrated); null when the flush kernel changed since",
         },
         "baselines": baselines,
+        "sketch_error": approx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -335,6 +342,43 @@ def flush_traffic(name):
     if e is None or e["src_sha256"] != flush_src_digest():
         return None
     return e["bytes"]
+
+
+def sketch_error(cfg, li, src, pool, steps):
+    """Relative L2 error of the sketched read against the exact read on the
+    same state and inputs: one fresh layer runs the sketch path (prime, read,
+    flush when due), another the ReplaySSM step, whose outputs are exact.
+    Synthetic states and queries have no low-rank structure, so this is far
+    from the pages' figures on model states; it is reported, not gated."""
+    import numpy as np
+    import torch
+    from ssm_decode_amd import abi, feed
+    from ssm_decode_amd.layer import DeviceStep
+    ls, lr = feed.make_layer(cfg, li), feed.make_layer(cfg, li)
+    ls.S.copy_(src.S)
+    lr.S.copy_(src.S)
+    assert feed.prime(ls, li) == 0
+    lr.count.copy_(torch.from_numpy(li.count0).to(lr.count.device))
+    os_, or_ = ls.new_step().o, lr.new_step().o
+    errs, flush_errs = [], []
+    for t in range(steps):
+        p = pool[t % len(pool)]
+        ss = DeviceStep(p.q, p.k, p.v, p.gate, p.beta, os_).struct()
+        sr = DeviceStep(p.q, p.k, p.v, p.gate, p.beta, or_).struct()
+        assert abi.sketchssm_read(ls.layer_struct, ls.buffers_struct, ss, None) == 0
+        due = bool((ls.count == cfg.window).any().item())
+        if due:
+            assert abi.sketchssm_flush(ls.layer_struct, ls.buffers_struct, ss, abi.SKSSM_FLUSH_DUE, None) == 0
+        assert abi.sketchssm_replay_step(lr.layer_struct, lr.buffers_struct, sr, None) == 0
+        a, b = os_.double(), or_.double()
+        e = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+        (flush_errs if due and not cfg.ragged else errs).append(e)
+    del ls, lr
+    out = {"rel_l2_mean": float(np.mean(errs)), "rel_l2_max": float(np.max(errs)),
+           "steps": steps, "against": "ReplaySSM step (exact read), same state and inputs"}
+    if flush_errs:
+        out["flush_steps_rel_l2_max"] = float(np.max(flush_errs))
+    return out
 
 
 def cpu_baseline(cfg, li, n_seq, windows):

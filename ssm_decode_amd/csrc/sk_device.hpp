@@ -184,6 +184,41 @@ __device__ __forceinline__ void tr_reduce(float (&a)[N], int lane) {
   }
 }
 
+// ------------------------------------------------------- buffer resources
+// A raw buffer over [base, base + bytes): a load or store addresses it with
+// one 32-bit lane offset (VGPR) plus a wave-uniform offset (SGPR), so a tile
+// read row by row keeps a single address register per lane instead of one
+// 64-bit pointer per row; accesses past the end are dropped by the hardware.
+// Descriptor word 3 is the gfx9 raw-buffer format (0x00020000).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <int N>
+__device__ __forceinline__ void buf_ld(__amdgpu_buffer_rsrc_t r, int voff, int soff, float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "buf_ld: 2 or 4 floats");
+  if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
+    x[2] = __uint_as_float(v[2]); x[3] = __uint_as_float(v[3]);
+  }
+}
+template <int N>
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "buf_st: 2 or 4 floats");
+  if constexpr (N == 2) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 v = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+  } else {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+  }
+}
+
 // ---------------------------------------------------------- DPP reductions
 // Data-parallel-primitive moves read a neighbour lane's register inside the
 // VALU instruction (no LDS permute, no address arithmetic).  Control codes

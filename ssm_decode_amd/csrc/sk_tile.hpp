@@ -102,6 +102,12 @@ __device__ __forceinline__ void unpack(const uint4& r, float (&x)[8], const floa
   x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
 }
 
+// Which tile kernels address the state through a buffer resource.
+template <int FAM, int MODE>
+struct STATE_BUFFER {
+  static constexpr bool value = FAM != FAM_M2 && MODE == MODE_FLUSH;
+};
+
 // D += A B for one 16x16x4 fp32 block (A: lane holds A[lane%16][lane/16],
 // B: lane holds B[lane/16][lane%16], D: lane holds D[4(lane/16)+v][lane%16]).
 __device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
@@ -249,19 +255,27 @@ tile_kernel(Params p) {
   }
 
   // ------------------------------------------------ issue the state loads
+  // State addressing.  As a buffer (delta-rule flush): the lane offset (rows
+  // 4 rg.., the lane's columns) in one VGPR and the row-block offset in an
+  // SGPR, which frees the registers of one 64-bit pointer per row.  As
+  // plain pointers elsewhere (the Mamba-2 kernels run best at their current
+  // occupancy).
+  constexpr bool SBUF = STATE_BUFFER<FAM, MODE>::value;
+  const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.S + bh * DK * DV, DK * DV * 4);
+  const int s_lane = (4 * rg * DV + colbase) * 4;
   f32x4v sacc[MB][NCC];
-  {
-    const float* Sg = p.S + bh * DK * DV + colbase;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x[NCC];
-        ldn<NCC>(Sg + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+    for (int v = 0; v < 4; ++v) {
+      float x[NCC];
+      if constexpr (SBUF)
+        buf_ld<NCC>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+      else
+        ldn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
 #pragma unroll
-        for (int c = 0; c < NCC; ++c) sacc[mb][c][v] = x[c];
-      }
-  }
+      for (int c = 0; c < NCC; ++c) sacc[mb][c][v] = x[c];
+    }
 
   // ------------------------------------------------ append (ReplaySSM)
   if (MODE == MODE_REPLAY) {
@@ -695,19 +709,17 @@ tile_kernel(Params p) {
 
   if (do_flush) {
     // ------------------------------------------------ store the state
-    float* Sw = p.S + bh * DK * DV + colbase;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float* dst = Sw + (size_t)(16 * mb + 4 * rg + v) * DV;
-        if constexpr (NCC == 4) {
-          const f32x4 v4 = {sacc[mb][0][v], sacc[mb][1][v], sacc[mb][2][v], sacc[mb][3][v]};
-          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(dst));
-        } else {
-          const float x[2] = {sacc[mb][0][v], sacc[mb][1][v]};
-          stn<2>(dst, x);
-        }
+        float x[NCC];
+#pragma unroll
+        for (int c = 0; c < NCC; ++c) x[c] = sacc[mb][c][v];
+        if constexpr (SBUF)
+          buf_st<NCC>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+        else
+          stn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
       }
 
     // --------------------------- sketch U = S^T P on the matrix cores
