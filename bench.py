@@ -322,8 +322,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2892519465,
-                "src_sha256": "0b4b12b7b87e8c0c1547989c0144bff898736958e540839230c4702c26a8efcc"},
+    "m2_b320": {"bytes": 2894185175,
+                "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
+    "gdn_b256": {"bytes": 1156134308,
+                 "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
+    "kda_b256": {"bytes": 1330868788,
+                 "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
