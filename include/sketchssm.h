@@ -161,10 +161,12 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
 
 /* Bytes of the workspace bufs->work that sketchssm_read needs for this layer
  * (0 when it needs none), or a negative SKSSM_E* code for an invalid layer.
- * Mamba-2 uses it for the query's coordinates in every head's sketch basis,
- * C_h q (B x R fp32), formed once per step for all heads of a B/C group
- * (the decay factor of the pulled-back query is applied afterwards).  The
- * caller allocates it; the library never does. */
+ * Mamba-2 uses it for what the heads of a B/C group share at a step: the
+ * query's coordinates in every head's sketch basis, C_h q (B x R fp32; the
+ * decay factor of the pulled-back query is applied afterwards), the dot
+ * products of the query with the group's buffered keys (B x G x W fp32) and
+ * the group's checked ring fill (B x G int32).  The caller allocates it; the
+ * library never does. */
 int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
 
 /* Library version (major * 10000 + minor * 100 + patch). */

@@ -26,11 +26,12 @@ struct Needs {
   bool S, U, Pt, C, ring, count, step_in, step_q, step_o, work;
 };
 
-// Workspace of a read: the Mamba-2 query coordinates cq [B][R] fp32.
+// Workspace of a Mamba-2 read (layout in sk_params.hpp): the query in every
+// head's basis, the key-query dot products and the checked ring fill.
 int64_t workspace_bytes(const sketchssm_layer* L) {
   if (L->family != SKSSM_MAMBA2) return 0;
-  const int64_t n = (int64_t)L->batch * L->rank_offsets_host[L->heads] * 4;
-  return (n + 255) / 256 * 256;
+  const sk::M2Work w(L->batch, L->rank_offsets_host[L->heads], L->qk_groups, L->window);
+  return (int64_t)w.total * 4;
 }
 
 int check_layer(const sketchssm_layer* L) {

@@ -29,11 +29,15 @@ static int launch_shape(int mode, const Params& p, hipStream_t st) {
   if (p.B <= 0 || p.H <= 0) return 0;
   if (mode == MODE_READ) {
     if (FAM == FAM_M2) {
-      hipLaunchKernelGGL((m2_cq_kernel<DK, AT>), dim3((p.B + CQ_NB - 1) / CQ_NB, p.G, CQ_ZBLOCKS), dim3(CQ_THREADS), 0, st, p);
-      if (p.W <= 16)
-        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 16>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
-      else
-        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 32>), dim3(p.B * p.G), dim3(M2ReadLanes<DK, DV>::LPH * p.HPG), 0, st, p);
+      const dim3 pgrid((p.B + CQ_NB - 1) / CQ_NB, p.G, CQ_ZBLOCKS + 1);
+      const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
+      if (p.W <= 16) {
+        hipLaunchKernelGGL((m2_prep_kernel<DK, AT, 16>), pgrid, dim3(CQ_THREADS), 0, st, p);
+        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 16>), rgrid, dim3(64), 0, st, p);
+      } else {
+        hipLaunchKernelGGL((m2_prep_kernel<DK, AT, 32>), pgrid, dim3(CQ_THREADS), 0, st, p);
+        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 32>), rgrid, dim3(64), 0, st, p);
+      }
     } else if (p.W <= 16) {
       hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, 16>), dim3(p.B * p.H), dim3(64), 0, st, p);
     } else {

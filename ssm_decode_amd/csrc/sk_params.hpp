@@ -35,6 +35,18 @@ struct Params {
   void* o;
 };
 
+// Workspace layout (floats): cq [B][R], then d [B][G][W], then n0 [B][G]
+// (int32), each region 256-byte aligned.
+struct M2Work {
+  size_t d, n0, total;
+  __host__ __device__ M2Work(int B, int R, int G, int W) {
+    const size_t cq = ((size_t)B * R + 63) / 64 * 64;
+    d = cq;
+    n0 = d + ((size_t)B * G * W + 63) / 64 * 64;
+    total = n0 + ((size_t)B * G + 63) / 64 * 64;
+  }
+};
+
 // Launch one kernel of `family` for `mode`; returns 0, or -2 when the shape
 // / dtype combination has no instantiation, or -5 on a launch error.
 int launch_m2(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);

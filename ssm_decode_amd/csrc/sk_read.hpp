@@ -9,23 +9,104 @@
 namespace sk {
 
 // ---------------------------------------------------------------- Mamba-2
+// The read of a Mamba-2 layer is two launches.
+//
+// m2_prep_kernel forms what the heads of a B/C group share, into the
+// workspace:
+//   cq[b][off_h + j] = (C_h q_b)_j        the query in each head's basis
+//   d[b][g][i]       = k_i . q_b          every buffered key and the step's own
+//   n0[b][g]         = the group's ring fill, or a negative error code when
+//                      the heads of the group disagree or the fill is out of
+//                      range
+// C is shared by all sequences, so one workgroup takes CQ_NB sequences of one
+// group and reads each row of C once.
+//
+// m2_read_kernel then needs no keys, no queries and no exchange between
+// heads: one wave per (sequence, group, block of four heads), with
+//   q~ = D q, D = prod_i a_i;   o_buf = sum_i w_i d_i v_i, w_i = dt_i prod_{t>i} a_t
+//   o  = D * U_h cq_h + o_buf
 constexpr int M2R_MAXHPG = 16;     // heads per B/C group (at most)
-// The query's coordinates in each head's sketch basis, before the decay:
-// cq[b][off_h + j] = (C_h q_b)_j, fp32, for every sequence and coefficient
-// row.  C is shared by every sequence, so one workgroup takes a block of
-// CQ_NB sequences, one B/C group and a block of CQ_ROWS of the group's
-// coefficient rows, and reads those rows of C once: CQ_LPR lanes hold one
-// row in registers, each forming the dot products of its segment with every
-// sequence's query (staged in LDS).  The coefficient rows are loaded first,
-// and every load is issued before the first wait.
-constexpr int CQ_NB = 8;           // sequences per workgroup
+constexpr int CQ_NB = 8;           // sequences per prep workgroup
 constexpr int CQ_THREADS = 256;
 constexpr int CQ_LPR = 4;          // lanes per coefficient row
 constexpr int CQ_ROWS = CQ_THREADS / CQ_LPR;
 constexpr int CQ_ZBLOCKS = (M2R_MAXHPG * 16 + CQ_ROWS - 1) / CQ_ROWS;
+constexpr int DOT_LPP = 4;         // lanes per (sequence, slot) dot product
 
-template <int DK, typename AT>
-__global__ void __launch_bounds__(CQ_THREADS) m2_cq_kernel(Params p) {
+template <int DK, typename AT, int WMAX>
+__device__ __forceinline__ void m2_prep_dots(const Params& p) {
+  constexpr int SEGD = DK / DOT_LPP;               // key elements per lane
+  constexpr int PPP = CQ_THREADS / DOT_LPP;        // pairs per pass
+  constexpr int PASSES = (CQ_NB * WMAX + PPP - 1) / PPP;
+  static_assert(SEGD % 8 == 0 || SEGD == 4, "key segments are 8-element (or 4) chunks");
+  const int tid = threadIdx.x;
+  const int qt = tid & (DOT_LPP - 1);
+  const int g = blockIdx.y;
+  const int b0 = blockIdx.x * CQ_NB;
+  const int nb = min(CQ_NB, p.B - b0);
+  const int W = p.W, HPG = p.HPG;
+  const M2Work wl(p.B, p.R, p.G, W);
+  float* dws = reinterpret_cast<float*>(p.work) + wl.d;
+  int* n0ws = reinterpret_cast<int*>(reinterpret_cast<float*>(p.work) + wl.n0);
+
+  // the group's ring fill per sequence: row bb (16 lanes) reads the counts
+  // of the group's heads; they must agree and lie in [0, W)
+  __shared__ int s_n0[CQ_NB];
+  {
+    const int bb = tid >> 4, l = tid & 15;
+    int c = 0;
+    if (bb < nb && l < HPG) c = p.count[(size_t)(b0 + bb) * p.H + g * HPG + l];
+    const int c0 = __shfl(c, 0, 16);
+    int bad = (l < HPG && c != c0) ? ERRBIT_GROUP : 0;
+    if (c0 < 0 || c0 >= W) bad |= ERRBIT_COUNT;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) bad |= __shfl_xor(bad, m, 16);
+    if (l == 0 && bb < CQ_NB) {
+      s_n0[bb] = (bb < nb && !bad) ? c0 : 0;     // clamped into the ring
+      if (bb < nb) n0ws[(size_t)(b0 + bb) * p.G + g] = bad ? -bad : c0;
+    }
+  }
+  __syncthreads();
+  const AT* kin = reinterpret_cast<const AT*>(p.k);
+  const AT* rk = reinterpret_cast<const AT*>(p.rk);
+  const AT* q = reinterpret_cast<const AT*>(p.q);
+  // issue every key and query segment load, then the dot products
+  VecN<AT, SEGD> kv[PASSES], qv[PASSES];
+  int pb[PASSES], pi[PASSES], pn0[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int pair = ps * PPP + (tid >> 2);
+    const int bb = pair / WMAX, i = pair - bb * WMAX;
+    const int n0 = s_n0[bb < CQ_NB ? bb : 0];
+    pb[ps] = bb; pi[ps] = i; pn0[ps] = n0;
+    const size_t bgi = (size_t)(b0 + (bb < nb ? bb : 0)) * p.G + g;
+    const AT* kp = (i < n0) ? rk + (bgi * W + i) * DK : kin + bgi * DK;
+    kv[ps] = ldraw<SEGD>(kp + qt * SEGD);
+    qv[ps] = ldraw<SEGD>(q + bgi * DK + qt * SEGD);
+  }
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < SEGD; e += 2) {
+      a0 += vget(kv[ps], e) * vget(qv[ps], e);
+      a1 += vget(kv[ps], e + 1) * vget(qv[ps], e + 1);
+    }
+    float d = a0 + a1;
+    d += dpp_f<0xB1>(d, 0.f);                      // quad sum: the pair's four lanes
+    d += dpp_f<0x4E>(d, 0.f);
+    const int bb = pb[ps], i = pi[ps];
+    if (qt == 0 && bb < nb && i <= pn0[ps])
+      dws[((size_t)(b0 + bb) * p.G + g) * W + i] = d;
+  }
+}
+
+template <int DK, typename AT, int WMAX>
+__global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
+  if (blockIdx.z == CQ_ZBLOCKS) {                  // uniform: the dot-product block
+    m2_prep_dots<DK, AT, WMAX>(p);
+    return;
+  }
   constexpr int SEGC = DK / CQ_LPR;              // row elements per lane
   constexpr int QCH = CQ_NB * DK / 4;            // 4-element query chunks per block
   constexpr int QIT = (QCH + CQ_THREADS - 1) / CQ_THREADS;
@@ -83,156 +164,104 @@ __global__ void __launch_bounds__(CQ_THREADS) m2_cq_kernel(Params p) {
   }
 }
 
-// Sketched read: one workgroup per (sequence, B/C group), LPH lanes per head
-// of the group.  The group's heads share k and q, so the dot products
-// d_i = k_i . q are formed once per workgroup.  For head h with n entries
-// (the step's own entry last):
-//   q~ = D q, D = prod_i a_i;   o_buf = sum_i w_i d_i v_i, w_i = dt_i prod_{t>i} a_t
-//   o  = D * U_h cq_h + o_buf,  cq_h = C_h q (from m2_cq_kernel)
-// Lane s of a head holds the q/k segment s (DK/LPH elements) for the dot
-// products, ring slots s*SPL.. for the decay scan, and output columns
-// s*CPL.. .  The loads are issued in the order their values are needed (the
-// memory counter retires them in order): step inputs, cq, the ring keys and
-// gates, then the sketch rows and ring values, which stay packed in
-// registers until the output sum.  The append stores the step's entry from
-// the registers that hold it.
-#ifndef SK_M2R_LPH
-#define SK_M2R_LPH 16              // lanes per head
-#endif
-constexpr int M2R_LPH = SK_M2R_LPH;
-
-// lanes per head for a head shape (at least one key element and one output
-// column per lane)
-template <int DK, int DV>
-struct M2ReadLanes {
-  static constexpr int v0 = M2R_LPH < DK ? M2R_LPH : DK;
-  static constexpr int LPH = v0 < DV ? v0 : DV;
-};
-
 template <int N, typename T>
 __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
   *reinterpret_cast<VecN<T, N>*>(p) = x;
 }
 
+// Sketched read: one wave per (sequence, group, block of M2R_HPW heads), 16
+// lanes per head (one DPP row).  Lane s of a head holds ring slots s*SPL..
+// for the decay scan, coefficient j = s, and output columns s*CPL.. .  The
+// ring fill comes from the prep kernel's workspace; then every load is
+// issued before the first wait: slot gates and dot products, the head's cq
+// entry, then a fixed number of sketch-row and ring-value loads (rows past
+// the rank or the fill re-read the last valid row, an L1 hit).  The
+// per-slot coefficients w_i d_i and the cq entries are exchanged within the
+// head's row through LDS (a wave reads what its own lanes wrote).
+constexpr int M2R_LPH = 16;        // lanes per head
+constexpr int M2R_HPW = 64 / M2R_LPH;   // heads per wave
+
+inline int m2_read_blocks(int B, int G, int HPG) {
+  return B * G * ((HPG + M2R_HPW - 1) / M2R_HPW);
+}
+
 template <int DK, int DV, typename AT, typename UT, int WMAX>
-__global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_read_kernel(Params p) {
-  constexpr int LPH = M2ReadLanes<DK, DV>::LPH;
-  constexpr int LB = ilog2c(LPH);
-  constexpr int SEG = DK / LPH;                  // key / query elements per lane
+__global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
+  constexpr int LPH = M2R_LPH;
+  constexpr int HPW = M2R_HPW;
+  constexpr int SEG = DK / LPH;                  // key elements per lane (append)
   constexpr int CPL = DV / LPH;                  // output columns per lane
-  constexpr int SPL = WMAX >= LPH ? WMAX / LPH : 1;  // ring slots per lane in the decay scan
-  static_assert(SEG >= 1 && CPL >= 1, "head dims too small for the lane split");
-  static_assert(LPH == 16, "a head is one 16-lane DPP row (and one cq row per thread)");
-  __shared__ float s_d[WMAX];                    // d_i = k_i . q
-  __shared__ float s_c[M2R_MAXHPG * 16];         // cq rows of the group
-  __shared__ __align__(16) float s_e[M2R_MAXHPG * WMAX];  // w_i d_i per head
+  constexpr int SPL = WMAX / LPH;                // ring slots per lane in the decay scan
+  static_assert(SEG >= 1 && CPL >= 1 && SPL >= 1, "head dims too small for the lane split");
+  __shared__ __align__(16) float s_e[HPW * WMAX];  // w_i d_i per head
+  __shared__ __align__(16) float s_c[HPW * 16];    // cq entries per head
 
+  const int wpg = (p.HPG + HPW - 1) / HPW;
+  const int item = blockIdx.x;
+  const int bgi = item / wpg;
+  const int wq = item - bgi * wpg;
   const int tid = threadIdx.x;
-  const int hh = tid >> LB;                      // head within the group
-  const int s = tid & (LPH - 1);
+  const int hh = tid >> 4;                       // head row of the wave
+  const int s = tid & 15;
   const int W = p.W, HPG = p.HPG;
-  const int b = blockIdx.x / p.G;
-  const int g = blockIdx.x - b * p.G;
-  const int h0 = g * HPG;
-  const int h = h0 + hh;
-  const size_t bg = (size_t)b * p.G + g;
+  const int b = bgi / p.G;
+  const int g = bgi - b * p.G;
+  const int hw = wq * HPW + hh;                  // head within the group
+  const bool hv = hw < HPG;
+  const int h = g * HPG + (hv ? hw : 0);
+  const size_t bg = (size_t)bgi;
   const size_t bh = (size_t)b * p.H + h;
+  const M2Work wl(p.B, p.R, p.G, W);
 
-  // ---------------------------------------------------- ring counts
-  const int n0g = p.count[(size_t)b * p.H + h0];  // the group's fill (uniform)
-  const int mine = p.count[bh];
+  // ------------------------------- ring fill (checked by the prep kernel)
+  const int n0c = reinterpret_cast<const int*>(reinterpret_cast<const float*>(p.work) + wl.n0)[bg];
   const int off = p.off[h];
-  const int r = p.off[h + 1] - off;
-  const int roff0 = p.off[h0];
-  const int rows = p.off[h0 + HPG] - roff0;
+  const int r = hv ? p.off[h + 1] - off : 0;
   const float Ah = p.A[h];
-  int bad = (n0g < 0 || n0g >= W) ? ERRBIT_COUNT : 0;
-  const int n0 = (n0g < 0 || n0g >= W) ? 0 : n0g; // in range for every address below
+  const int n0 = n0c < 0 ? 0 : n0c;              // in range for every address below
   const int n = n0 + 1;
-  // keep the count and offset loads ahead of every other load: the addresses
-  // below depend on them and the memory counter retires loads in order
   __builtin_amdgcn_sched_barrier(0);
 
-  const AT* q = reinterpret_cast<const AT*>(p.q) + bg * DK;
   const AT* kin = reinterpret_cast<const AT*>(p.k) + bg * DK;
   const AT* vin = reinterpret_cast<const AT*>(p.v) + bh * DV;
   const AT* dtin = reinterpret_cast<const AT*>(p.gate) + bh;
-  const AT* ring_k = reinterpret_cast<const AT*>(p.rk) + bg * W * DK;
   const AT* ring_v = reinterpret_cast<const AT*>(p.rv) + bh * W * DV;
   const AT* ring_dt = reinterpret_cast<const AT*>(p.rg) + bh * W;
+  const float* dws = reinterpret_cast<const float*>(p.work) + wl.d + bg * W;
 
   // the step's own entry (kept for the append)
   const VecN<AT, SEG> kcur = ldraw<SEG>(kin + s * SEG);
   const VecN<AT, CPL> vcur = ldraw<CPL>(vin + s * CPL);
   const AT dtcur = dtin[0];
 
-  if (n < W) {
+  if (n < W && n0c >= 0) {                       // uniform
     // ---------------------------------------------- issue the loads
-    // (loads are unconditional, from clamped indices, and their values are
-    // selected where used: a load behind a branch with a default value
-    // makes the wave wait for it inside the branch)
-    float qs[SEG];
-    ldn<SEG>(q + s * SEG, qs);
-    const float cqv = reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + roff0 + min(tid, rows - 1)];
-    // key of the first ring slot this head takes for the dot products
-    const VecN<AT, SEG> k0r = ldraw<SEG>(ring_k + (size_t)(hh < n0 ? hh : 0) * DK + s * SEG);
     AT dtr[SPL];
+    float dr[SPL];
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
       const int i = s * SPL + u;
       dtr[u] = ring_dt[i < n0 ? i : 0];
+      dr[u] = dws[i <= n0 ? i : 0];
     }
-    // sketch rows and ring values of the earlier entries (HBM).  Every row
-    // slot is loaded, rows past the head's rank or the ring fill from the
-    // last valid row (an L1 hit, no extra HBM traffic), so the number of
-    // loads in flight is fixed and the waits below retire only the loads
-    // they need.
+    const float cqv = reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + off + (s < r ? s : 0)];
     VecN<UT, CPL> us[16];
     const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
+    const int jlast = r > 0 ? r - 1 : 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) us[j] = ldraw<CPL>(Ur + (size_t)min(j, r - 1) * DV);
+    for (int j = 0; j < 16; ++j) us[j] = ldraw<CPL>(Ur + (size_t)min(j, jlast) * DV);
     VecN<AT, CPL> vs[WMAX];
     const AT* rv0 = ring_v + s * CPL;
     const int ilast = n0 > 0 ? n0 - 1 : 0;
 #pragma unroll
     for (int i = 0; i < WMAX - 1; ++i) vs[i] = ldraw<CPL>(rv0 + (size_t)min(i, ilast) * DV);
 
-    float dts[SPL];
+    // -------------------------------- decays: suffix products per head
+    float dts[SPL], a[SPL], lp = 1.f;
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
       const int i = s * SPL + u;
       dts[u] = (i < n0) ? to_f32(dtr[u]) : (i == n0 ? to_f32(dtcur) : 0.f);
-    }
-    // d_i = k_i . q, slots spread over the group's heads (LPH lanes per slot)
-    if (hh < n) {
-      const VecN<AT, SEG> k0 = hh < n0 ? k0r : kcur;
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < SEG; ++e) d += vget(k0, e) * qs[e];
-      d = row16_sum(d);
-      if (s == 0) s_d[hh] = d;
-    }
-    for (int i = hh + HPG; i < n; i += HPG) {
-      float ks[SEG];
-      if (i < n0) {
-        ldn<SEG>(ring_k + (size_t)i * DK + s * SEG, ks);
-      } else {
-#pragma unroll
-        for (int e = 0; e < SEG; ++e) ks[e] = vget(kcur, e);
-      }
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < SEG; ++e) d += ks[e] * qs[e];
-      d = row16_sum(d);
-      if (s == 0) s_d[i] = d;
-    }
-    if (tid < rows) s_c[tid] = cqv;
-
-    // -------------------------------- decays: suffix products per head
-    float a[SPL], lp = 1.f;
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int i = s * SPL + u;
       a[u] = (i < n) ? m2_decay(dts[u], Ah) : 1.0f;
       lp *= a[u];
     }
@@ -245,48 +274,38 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
     incl *= dpp_f<0x108>(incl, 1.f);
     const float after = dpp_f<0x101>(incl, 1.f); // prod over lanes > s
     const float D = row16_prod(lp);
-    float w[SPL];
+    float* eh = s_e + hh * WMAX;
+    float* ch = s_c + hh * 16;
     {
       float suf = after;
 #pragma unroll
       for (int u = SPL - 1; u >= 0; --u) {
-        w[u] = dts[u] * suf;                        // dt_i prod_{t>i} a_t
+        const int i = s * SPL + u;
+        eh[i] = (i < n) ? dts[u] * suf * dr[u] : 0.f;   // w_i d_i
         suf *= a[u];
       }
     }
-    if (mine != n0g) bad |= ERRBIT_GROUP;
-    if (__syncthreads_or(bad)) {                   // s_d and s_c complete
-      if (s == 0 && bad) atomicOr(p.err, bad);
-      return;
-    }
-    // e_i = w_i d_i, exchanged within the head's row through LDS (a wave
-    // reads back what its own lanes wrote: LDS keeps a wave's order)
-    float* eh = s_e + hh * WMAX;
-#pragma unroll
-    for (int u = 0; u < SPL; ++u) {
-      const int i = s * SPL + u;
-      eh[i] = (i < n) ? w[u] * s_d[i] : 0.f;
-    }
+    ch[s] = cqv;
 
     // ------------------------------------------------------- output
     float acc[CPL], ob[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = ob[c] = 0.f;
-    const float* cme = s_c + (off - roff0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < r) {
-        const float cj = cme[j];
+        const float cj = ch[j];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] += cj * vget(us[j], c);
       }
     }
 #pragma unroll
     for (int i = 0; i < WMAX - 1; ++i) {
-      const float ei = eh[i];
-      if (i < n0)
+      if (i < n0) {
+        const float ei = eh[i];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) ob[c] += ei * vget(vs[i], c);
+      }
     }
     {
       const float ecur = eh[n0];
@@ -296,23 +315,23 @@ __global__ void __launch_bounds__((M2ReadLanes<DK, DV>::LPH * M2R_MAXHPG)) m2_re
     float out[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
-    stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
-  } else {
-    if (mine != n0g) bad |= ERRBIT_GROUP;
-    if (__syncthreads_or(bad)) {                   // pairs with the barrier above
-      if (s == 0 && bad) atomicOr(p.err, bad);
-      return;
-    }
+    if (hv) stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
+  }
+  if (n0c < 0) {                                 // the prep kernel found a bad group
+    if (tid == 0 && wq == 0) atomicOr(p.err, -n0c);
+    return;
   }
 
   // ------------------------------------------------------------ append
   AT* rk = reinterpret_cast<AT*>(p.rk) + (bg * W + n0) * DK;
   AT* rv = reinterpret_cast<AT*>(p.rv) + (bh * W + n0) * DV;
-  if (hh == 0) stv<SEG>(rk + s * SEG, kcur);
-  stv<CPL>(rv + s * CPL, vcur);
-  if (s == 0) {
-    reinterpret_cast<AT*>(p.rg)[bh * W + n0] = dtcur;
-    p.count[bh] = n;
+  if (wq == 0 && hh == 0) stv<SEG>(rk + s * SEG, kcur);
+  if (hv) {
+    stv<CPL>(rv + s * CPL, vcur);
+    if (s == 0) {
+      reinterpret_cast<AT*>(p.rg)[bh * W + n0] = dtcur;
+      p.count[bh] = n;
+    }
   }
 }
 

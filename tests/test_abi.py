@@ -141,12 +141,19 @@ def test_bad_flag(lib):
     assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, -1) == abi.SKSSM_EFLAG
 
 
+def _m2_work_bytes(B, R, G, W):
+    # the query in every head's basis [B][R], the key-query dot products
+    # [B][G][W] and the checked ring fill [B][G], 4 bytes each, every region
+    # rounded up to 256 bytes
+    a64 = lambda n: (n + 63) // 64 * 64
+    return 4 * (a64(B * R) + a64(B * G * W) + a64(B * G))
+
+
 def test_workspace_bytes(lib):
-    # Mamba-2: one fp32 per (sequence, coefficient row), rounded up to 256 bytes
-    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 256
+    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == _m2_work_bytes(2, 16, 4, 4) == 768
     off = np.concatenate([[0], np.cumsum(np.full(128, 8))]).astype(np.int32)
     L = _layer(off, batch=320, heads=128, groups=8, dk=128, dv=64, W=16)
-    assert abi.sketchssm_workspace_bytes(L) == 320 * 1024 * 4
+    assert abi.sketchssm_workspace_bytes(L) == _m2_work_bytes(320, 1024, 8, 16)
     for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
         assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == 0
     assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, W=0)) == abi.SKSSM_EDIM
