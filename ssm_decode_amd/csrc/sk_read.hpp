@@ -174,10 +174,11 @@ __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
 // for the decay scan, coefficient j = s, and output columns s*CPL.. .  The
 // ring fill comes from the prep kernel's workspace; then every load is
 // issued before the first wait: slot gates and dot products, the head's cq
-// entry, then a fixed number of sketch-row and ring-value loads (rows past
-// the rank or the fill re-read the last valid row, an L1 hit).  The
-// per-slot coefficients w_i d_i and the cq entries are exchanged within the
-// head's row through LDS (a wave reads what its own lanes wrote).
+// entry, then the head's r sketch rows and n0 ring values (the lean kernel
+// has nothing to overlap with them, so loads past the rank or the fill are
+// not issued).  The per-slot coefficients w_i d_i and the cq entries are
+// exchanged within the head's row through LDS (a wave reads what its own
+// lanes wrote).
 constexpr int M2R_LPH = 16;        // lanes per head
 constexpr int M2R_HPW = 64 / M2R_LPH;   // heads per wave
 
@@ -247,14 +248,14 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
     const float cqv = reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + off + (s < r ? s : 0)];
     VecN<UT, CPL> us[16];
     const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
-    const int jlast = r > 0 ? r - 1 : 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) us[j] = ldraw<CPL>(Ur + (size_t)min(j, jlast) * DV);
+    for (int j = 0; j < 16; ++j)
+      if (j < r) us[j] = ldraw<CPL>(Ur + (size_t)j * DV);
     VecN<AT, CPL> vs[WMAX];
     const AT* rv0 = ring_v + s * CPL;
-    const int ilast = n0 > 0 ? n0 - 1 : 0;
 #pragma unroll
-    for (int i = 0; i < WMAX - 1; ++i) vs[i] = ldraw<CPL>(rv0 + (size_t)min(i, ilast) * DV);
+    for (int i = 0; i < WMAX - 1; ++i)
+      if (i < n0) vs[i] = ldraw<CPL>(rv0 + (size_t)i * DV);
 
     // -------------------------------- decays: suffix products per head
     float dts[SPL], a[SPL], lp = 1.f;
