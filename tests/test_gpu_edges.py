@@ -219,3 +219,57 @@ def test_small_gates(family, power, seed):
             assert es <= 1e-5, (t, es)
     assert lay.error_word() == 0
     print(f"  gates^{power}: max rel-L2 o={worst_o:.2e} S={worst_s:.2e}")
+
+
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256"])
+def test_graph_replays_match_eager(name):
+    """The benchmark times its steps as a captured HIP graph.  A layer that
+    runs whole windows as graph replays (eager work and synchronisations in
+    between) stays bit-identical to a twin layer run eagerly with the same
+    inputs: outputs, states, sketches and counts after every replay."""
+    import synth
+    from ssm_decode_amd import abi, feed
+    cfg = CONFIGS[name].with_(name=name + "_graph", batch=4, ragged=True)
+    W = cfg.window
+    li = synth.make_layer_inputs(cfg)
+    layers = []
+    for _ in range(2):
+        lay = feed.make_layer(cfg, li)
+        feed.fill_state(lay, cfg, numpy_all=True)
+        assert feed.prime(lay, li) == 0
+        layers.append(lay)
+    ge, eg = layers
+    steps = [ge.new_step() for _ in range(W)]
+    for t, st in enumerate(steps):
+        feed.fill_step(st, cfg, t, numpy_all=True)
+    outs_g = [ge.new_step().o for _ in range(W)]
+    outs_e = [eg.new_step().o for _ in range(W)]
+    from ssm_decode_amd.layer import DeviceStep
+
+    def run(lay, outs, handle):
+        for t, st in enumerate(steps):
+            ds = DeviceStep(st.q, st.k, st.v, st.gate, st.beta, outs[t]).struct()
+            assert abi.sketchssm_read(lay.layer_struct, lay.buffers_struct, ds, handle) == 0
+            assert abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, ds, abi.SKSSM_FLUSH_DUE,
+                                       handle) == 0
+
+    import ctypes
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(ge, outs_g, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    # capture does not execute: both layers are still at the primed state
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        run(eg, outs_e, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        _ = (ge.S.sum() + eg.S.sum()).item()          # eager work between replays
+        for t in range(W):
+            assert torch.equal(outs_g[t], outs_e[t]), (rep, t)
+        assert torch.equal(ge.S, eg.S), rep
+        assert torch.equal(ge.U, eg.U), rep
+        assert torch.equal(ge.count, eg.count), rep
+        assert torch.equal(ge.ring_v, eg.ring_v), rep
+    assert ge.error_word() == 0 and eg.error_word() == 0
