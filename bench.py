@@ -322,12 +322,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2894185175,
-                "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
-    "gdn_b256": {"bytes": 1156134308,
-                 "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
-    "kda_b256": {"bytes": 1330868788,
-                 "src_sha256": "b455d903ec9a4adf3e32e6e68ecccf287fb3d495ec7dce2436b7220d5b488b3d"},
+    "m2_b320": {"bytes": 2894228141,
+                "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
+    "gdn_b256": {"bytes": 1156135646,
+                 "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
+    "kda_b256": {"bytes": 1330880768,
+                 "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
