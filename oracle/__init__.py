@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "_build", "libsketchssm_oracle.so")
 
 FAMILY = {"mamba2": 0, "gdn": 1, "kda": 2}
 STORE = {"exact": 0, "f32": 1, "bf16": 2}
+COEF = {"fixed": 0, "state": 1}
 ERR_COUNT = 1
 
 
@@ -40,7 +41,7 @@ def build(force: bool = True) -> str:
 class _Layer(C.Structure):
     _fields_ = [("family", C.c_int), ("dk", C.c_int), ("dv", C.c_int), ("W", C.c_int),
                 ("rmax", C.c_int), ("state_store", C.c_int), ("sketch_store", C.c_int),
-                ("out_store", C.c_int)]
+                ("out_store", C.c_int), ("coef_mode", C.c_int), ("coef_ridge", C.c_double)]
 
 
 _DP = C.POINTER(C.c_double)
@@ -104,13 +105,17 @@ class OracleLayer:
     tiles: [n, 2] array of (b, h); S0: [n][dk][dv] initial state of those
     tiles; stores: rounding at the state / sketch / output stores ("exact",
     "f32", "bf16"); qk_groups: heads per B/C group for the k/q gather.
+    coef: "fixed" reads the per-head table Cmap; "state" makes every flush
+    write each tile's own map from its new state (Cmap is then ignored) with
+    the relative ridge ``ridge``; the map is stored in the sketch dtype.
     """
 
     def __init__(self, family: str, dk: int, dv: int, W: int, ranks: np.ndarray,
                  offsets: np.ndarray, Pt: np.ndarray, Cmap: np.ndarray,
                  A: Optional[np.ndarray], tiles: np.ndarray, S0: np.ndarray,
                  heads: int, qk_groups: int, state_store="f32", sketch_store="f32",
-                 out_store="f32", count0: Optional[np.ndarray] = None):
+                 out_store="f32", count0: Optional[np.ndarray] = None,
+                 coef: str = "fixed", ridge: float = 0.0):
         self.family, self.dk, self.dv, self.W = family, dk, dv, W
         self.tiles = np.ascontiguousarray(np.asarray(tiles, dtype=np.int64).reshape(-1, 2))
         n = len(self.tiles)
@@ -125,7 +130,8 @@ class OracleLayer:
         for i, h in enumerate(hh):
             r = int(ranks[h])
             self.Pt[i, :r] = Pt[offsets[h]:offsets[h] + r]
-            self.C[i, :r] = Cmap[offsets[h]:offsets[h] + r]
+            if coef == "fixed":
+                self.C[i, :r] = Cmap[offsets[h]:offsets[h] + r]
         self.A = None if A is None else np.ascontiguousarray(np.asarray(A, dtype=np.float64)[hh])
         self.S = np.ascontiguousarray(np.asarray(S0, dtype=np.float64).reshape(n, dk, dv)).copy()
         self.U = np.zeros((n, self.rmax, dv))
@@ -138,7 +144,7 @@ class OracleLayer:
         self.count = np.zeros(n, dtype=np.int32) if count0 is None else \
             np.ascontiguousarray(np.asarray(count0, dtype=np.int32).reshape(n)).copy()
         self.L = _Layer(FAMILY[family], dk, dv, W, self.rmax, STORE[state_store],
-                        STORE[sketch_store], STORE[out_store])
+                        STORE[sketch_store], STORE[out_store], COEF[coef], float(ridge))
 
     # ------------------------------------------------------------------
     def _tiles_struct(self):

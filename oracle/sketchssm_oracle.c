@@ -20,7 +20,12 @@
  *    transitions, so that the state-read term is S_0^T q~_t (paper Sec. 3.2,
  *    project page error objective; Mamba-2 has decay only, App. C.1);
  *  - ReplaySSM: buffered writes, full-state read each step (paper Sec. 1-2,
- *    App. D).
+ *    App. D);
+ *  - the coefficient map C is either a fixed per-head table (the paper's
+ *    fixed-coefficient rule, App. G) or, as the project page's per-window
+ *    flush panel has it, the state-dependent map C = (U^T U)^+ U^T S0^T
+ *    refreshed at every flush (paper App. A.2.1; App. A.2.2 names the
+ *    regularised solve that is written out here).
  *
  * Per family (the Mamba-2 write term, the KDA operator order and the gate
  * dtypes are readings taken where the pages leave the step open):
@@ -44,6 +49,7 @@
 enum { ORC_MAMBA2 = 0, ORC_GDN = 1, ORC_KDA = 2 };
 enum { ORC_STORE_EXACT = 0, ORC_STORE_F32 = 1, ORC_STORE_BF16 = 2 };
 enum { ORC_OK = 0, ORC_ERR_COUNT = 1 };
+enum { ORC_COEF_FIXED = 0, ORC_COEF_STATE = 1 };
 
 typedef struct {
     int family;
@@ -52,6 +58,9 @@ typedef struct {
     int state_store;   /* EXACT or F32 */
     int sketch_store;  /* EXACT, F32 or BF16 */
     int out_store;     /* EXACT, F32 or BF16 */
+    int coef_mode;     /* ORC_COEF_FIXED: C is an input table;
+                          ORC_COEF_STATE: the flush writes C from the new state */
+    double coef_ridge; /* ORC_COEF_STATE: ridge relative to the mean Gram eigenvalue */
 } orc_layer;
 
 /* n independent tiles; every array is indexed by tile first. */
@@ -61,7 +70,8 @@ typedef struct {
     double* S;           /* [n][dk][dv] stored state */
     double* U;           /* [n][rmax][dv] stored sketch, row j = u_j = S^T p_j */
     const double* Pt;    /* [n][rmax][dk] row j = column j of P_h (basis) */
-    const double* C;     /* [n][rmax][dk] row j = row j of C_h */
+    double* C;           /* [n][rmax][dk] row j = row j of the tile's coefficient map
+                            (written by the flush in ORC_COEF_STATE mode) */
     const double* A;     /* [n] Mamba-2 A_h (unused otherwise) */
     double* rk;          /* [n][W][dk] ring keys */
     double* rv;          /* [n][W][dv] ring values */
@@ -257,6 +267,75 @@ static void build_sketch(const orc_layer* L, orc_tiles* T, int i, const double* 
     free(u);
 }
 
+/* State-dependent coefficient map of tile i from its updated state S (dk x dv,
+ * fp64) and the sketch rows u_j just stored (r x dv, as rounded at the store).
+ * The non-flush read wants the coefficients c that best reproduce S^T q~ from
+ * the stored sketch vectors, min_c |S^T q~ - sum_j c_j u_j|^2 (+ ridge), for
+ * every q~; their normal equations give c = C q~ with
+ *     G = [u_j . u_l]              the r x r Gram matrix of the sketch vectors,
+ *     Y = [u_j . S[m, :]]          r x dk (the pages' U^T S0^T),
+ *     (G + lambda I) C = Y,        lambda = ridge * trace(G) / r,
+ * which is the pages' pseudoinverse form as ridge -> 0 when the u_j are
+ * independent.  Solved by a Cholesky factorisation; C is stored in the
+ * sketch dtype.  A zero sketch (trace 0) gives C = 0. */
+static void build_coef_map(const orc_layer* L, orc_tiles* T, int i, const double* S,
+                           const double* S_before) {
+    const int r = T->rank[i], dk = L->dk, dv = L->dv;
+    double* Cout = TC(T, L, i);
+    const double* Uh = TU(T, L, i);
+    double* u = NULL;
+    if (g_mutation == 12) {                    /* planted: sketch before rounding */
+        u = (double*)malloc(sizeof(double) * (size_t)r * dv);
+        const double* P = TP(T, L, i);
+        for (int j = 0; j < r; ++j) state_read(L, S, P + (size_t)j * dk, u + (size_t)j * dv);
+        Uh = u;
+    }
+    const double* Sy = (g_mutation == 13) ? S_before : S;   /* planted: old state */
+    double* G = (double*)malloc(sizeof(double) * (size_t)r * r);
+    double* Y = (double*)malloc(sizeof(double) * (size_t)r * dk);
+    double tr = 0.0;
+    for (int j = 0; j < r; ++j) {
+        for (int l = 0; l < r; ++l) G[j * r + l] = dot(Uh + (size_t)j * dv, Uh + (size_t)l * dv, dv);
+        tr += G[j * r + j];
+        for (int m = 0; m < dk; ++m) Y[(size_t)j * dk + m] = dot(Uh + (size_t)j * dv, Sy + (size_t)m * dv, dv);
+    }
+    if (tr == 0.0) {
+        for (int e = 0; e < r * dk; ++e) Cout[e] = 0.0;
+    } else {
+        const double lambda = (g_mutation == 11) ? 0.0 : L->coef_ridge * tr / r;
+        for (int j = 0; j < r; ++j) G[j * r + j] += lambda;
+        /* G = R R^T, R lower triangular, written over the lower half of G */
+        for (int j = 0; j < r; ++j) {
+            double d = G[j * r + j];
+            for (int l = 0; l < j; ++l) d -= G[j * r + l] * G[j * r + l];
+            d = sqrt(d);
+            G[j * r + j] = d;
+            for (int t = j + 1; t < r; ++t) {
+                double x = G[t * r + j];
+                for (int l = 0; l < j; ++l) x -= G[t * r + l] * G[j * r + l];
+                G[t * r + j] = x / d;
+            }
+        }
+        /* every column of Y: solve R z = y, then R^T c = z */
+        for (int m = 0; m < dk; ++m) {
+            for (int j = 0; j < r; ++j) {
+                double x = Y[(size_t)j * dk + m];
+                for (int l = 0; l < j; ++l) x -= G[j * r + l] * Y[(size_t)l * dk + m];
+                Y[(size_t)j * dk + m] = x / G[j * r + j];
+            }
+            for (int j = r - 1; j >= 0; --j) {
+                double x = Y[(size_t)j * dk + m];
+                for (int l = j + 1; l < r; ++l) x -= G[l * r + j] * Y[(size_t)l * dk + m];
+                Y[(size_t)j * dk + m] = x / G[j * r + j];
+            }
+        }
+        for (int e = 0; e < r * dk; ++e) Cout[e] = store(L->sketch_store, Y[e]);
+    }
+    free(G);
+    free(Y);
+    free(u);
+}
+
 static void write_out(const orc_layer* L, const orc_step* st, int i, const double* o) {
     for (int n = 0; n < L->dv; ++n) st->o[(size_t)i * L->dv + n] = store(L->out_store, o[n]);
 }
@@ -302,6 +381,7 @@ int orc_flush(const orc_layer* L, orc_tiles* T, const orc_step* st, int all) {
         apply_ring(L, T, i, n, S);
         store_state(L, T, i, S);
         build_sketch(L, T, i, S);
+        if (L->coef_mode == ORC_COEF_STATE) build_coef_map(L, T, i, S, S0);
         if (st && st->o) {
             state_read(L, g_mutation == 10 ? S0 : S, st->q + (size_t)i * L->dk, o);
             write_out(L, st, i, o);
@@ -387,7 +467,7 @@ int orc_replay_step(const orc_layer* L, orc_tiles* T, const orc_step* st) {
     return err;
 }
 
-int orc_abi_version(void) { return 1; }
+int orc_abi_version(void) { return 2; }
 
 #ifdef _OPENMP
 #include <omp.h>
