@@ -15,6 +15,12 @@
  *     buffered transitions; S is not read (project page, per-step non-flush
  *     panel; paper Sec. 3.2 and App. C.1).
  *
+ * The coefficient map C is either a fixed per-head table the caller supplies
+ * (the paper's fixed-coefficient rule, App. G) or the state-dependent map the
+ * flush forms for every (sequence, head) tile from its new state,
+ * C = (U^T U + lambda I)^{-1} U^T S^T with U the stored sketch (project page,
+ * per-window flush panel; paper App. A.2.1-A.2.2).
+ *
  * Two baselines share the layout: the standard full-state step (read and
  * write S every step; project page "01 / The idea", S_t = M_t S_{t-1} + B_t,
  * o_t = S_t^T q_t) and ReplaySSM (buffered writes, full-state read every
@@ -65,6 +71,10 @@ extern "C" {
 #define SKSSM_F32 0
 #define SKSSM_BF16 1
 
+/* coefficient maps */
+#define SKSSM_COEF_FIXED 0 /* bufs->C: one fp32 map per head, shared by all sequences */
+#define SKSSM_COEF_STATE 1 /* bufs->Cstate: one map per (sequence, head), written by the flush */
+
 /* flush flags */
 #define SKSSM_FLUSH_DUE 0 /* flush tiles whose ring holds W entries */
 #define SKSSM_FLUSH_ALL 1 /* flush every tile (prime U, or retire sequences) */
@@ -74,7 +84,7 @@ extern "C" {
 #define SKSSM_EINVAL -1  /* NULL or misaligned pointer (16-byte alignment) */
 #define SKSSM_EDIM -2    /* unsupported shape, W, ranks or rank table */
 #define SKSSM_EDTYPE -3  /* unsupported dtype combination */
-#define SKSSM_EFLAG -4   /* unknown flag */
+#define SKSSM_EFLAG -4   /* unknown flag or coefficient-map mode */
 #define SKSSM_ELAUNCH -5 /* kernel launch failed */
 
 /* bits OR-ed into *err by the kernels */
@@ -94,6 +104,10 @@ typedef struct {
   int32_t act_dtype;         /* dtype of q, k, v, o, Mamba-2 dt and the ring's k, v, dt */
   int32_t sketch_dtype;      /* dtype of U */
   const int32_t* rank_offsets_host; /* [H+1] host copy: exclusive prefix sum of r_h */
+  int32_t coef_map;          /* SKSSM_COEF_FIXED or SKSSM_COEF_STATE */
+  float coef_ridge;          /* SKSSM_COEF_STATE: ridge relative to the mean eigenvalue of
+                                the sketch's Gram matrix, lambda = coef_ridge * trace(G) / r_h;
+                                finite and > 0 (ignored for SKSSM_COEF_FIXED) */
 } sketchssm_layer;
 
 typedef struct {
@@ -101,7 +115,8 @@ typedef struct {
   void* U;                   /* [B][R][dv] sketch dtype, R = offsets[H]; rows
                                 off_h..off_h+r_h-1 hold u_j = S^T p_j of head h */
   const float* Pt;           /* [R][dk] fp32: row off_h + j = column j of P_h */
-  const float* C;            /* [R][dk] fp32: row off_h + j = row j of C_h (r_h x dk) */
+  const float* C;            /* SKSSM_COEF_FIXED: [R][dk] fp32: row off_h + j = row j of C_h
+                                (r_h x dk); NULL allowed for SKSSM_COEF_STATE */
   const int32_t* rank_offsets; /* [H+1] device copy of rank_offsets_host */
   void* ring_k;              /* [B][G][W][dk] act dtype */
   void* ring_v;              /* [B][H][W][dv] act dtype */
@@ -115,6 +130,9 @@ typedef struct {
   void* work;                /* workspace of sketchssm_workspace_bytes(layer) bytes (16-byte
                                 aligned; may be NULL when that is 0); scratch that a call
                                 overwrites, so calls sharing one workspace must be ordered */
+  void* Cstate;              /* SKSSM_COEF_STATE: [B][R][dk] sketch dtype; rows off_h..off_h+r_h-1
+                                of sequence b hold the map of tile (b, h), written by every
+                                flush of that tile (NULL allowed for SKSSM_COEF_FIXED) */
 } sketchssm_buffers;
 
 typedef struct {             /* one decode step */
@@ -131,8 +149,10 @@ typedef struct {             /* one decode step */
  * o^ = U c, plus the exact buffered contribution; paper Sec. 3.2 and
  * App. C.1 for q~).  For every tile: append the step's (k, v, gate, beta) at
  * ring slot count, count += 1; if count < W write o = U (C q~) + o_buf,
- * otherwise leave o for sketchssm_flush.  Never reads S.  Mamba-2 layers
- * need bufs->work (sketchssm_workspace_bytes). */
+ * otherwise leave o for sketchssm_flush.  Never reads S.  C is bufs->C
+ * (SKSSM_COEF_FIXED) or the tile's own map in bufs->Cstate, as its last
+ * flush wrote it (SKSSM_COEF_STATE).  Mamba-2 layers need bufs->work
+ * (sketchssm_workspace_bytes). */
 int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                    const sketchssm_step* step, void* hip_stream);
 
@@ -141,7 +161,12 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * SKSSM_FLUSH_DUE) or every tile (SKSSM_FLUSH_ALL): apply the count buffered
  * entries to S in order, write S, write U = S^T P from the updated state,
  * set count = 0 and, if step != NULL, write the exact output o = S^T q.
- * FLUSH_ALL with count == 0 primes U from the current state. */
+ * FLUSH_ALL with count == 0 primes U from the current state.
+ * SKSSM_COEF_STATE: also write the tile's map to bufs->Cstate, solved in
+ * fp32 from the sketch rows as stored (rounded to the sketch dtype) and the
+ * updated state: G = U_h U_h^T (r_h x r_h), Y = U_h S^T (r_h x dk),
+ * C = (G + lambda I)^{-1} Y, lambda = coef_ridge * trace(G) / r_h, stored in
+ * the sketch dtype (C = 0 when the sketch is zero). */
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,
                     void* hip_stream);

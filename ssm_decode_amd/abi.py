@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libsketchssm.so")
 SKSSM_MAMBA2, SKSSM_GDN, SKSSM_KDA = 0, 1, 2
 SKSSM_F32, SKSSM_BF16 = 0, 1
 SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL = 0, 1
+SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5
 SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP = 1, 2
 
@@ -29,14 +30,16 @@ class sketchssm_layer(C.Structure):
     _fields_ = [("family", C.c_int32), ("batch", C.c_int32), ("heads", C.c_int32),
                 ("qk_groups", C.c_int32), ("dk", C.c_int32), ("dv", C.c_int32),
                 ("window", C.c_int32), ("act_dtype", C.c_int32), ("sketch_dtype", C.c_int32),
-                ("rank_offsets_host", C.POINTER(C.c_int32))]
+                ("rank_offsets_host", C.POINTER(C.c_int32)), ("coef_map", C.c_int32),
+                ("coef_ridge", C.c_float)]
 
 
 class sketchssm_buffers(C.Structure):
     _fields_ = [("S", C.c_void_p), ("U", C.c_void_p), ("Pt", C.c_void_p), ("C", C.c_void_p),
                 ("rank_offsets", C.c_void_p), ("ring_k", C.c_void_p), ("ring_v", C.c_void_p),
                 ("ring_gate", C.c_void_p), ("ring_beta", C.c_void_p), ("count", C.c_void_p),
-                ("A", C.c_void_p), ("err", C.c_void_p), ("work", C.c_void_p)]
+                ("A", C.c_void_p), ("err", C.c_void_p), ("work", C.c_void_p),
+                ("Cstate", C.c_void_p)]
 
 
 class sketchssm_step(C.Structure):

@@ -1,6 +1,7 @@
 // C ABI of the SketchSSM decode library: host-side validation and dispatch.
 // Every check runs before any HIP call, so an invalid call launches nothing
 // and writes nothing.
+#include <math.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -24,6 +25,7 @@ bool shape_supported(int dk, int dv) {
 // What a call needs from the buffers and the step.
 struct Needs {
   bool S, U, Pt, C, ring, count, step_in, step_q, step_o, work;
+  bool Cstate;   // writes (flush) or reads (read) the state-dependent maps
 };
 
 // Workspace of a Mamba-2 read (layout in sk_params.hpp): the query in every
@@ -48,6 +50,9 @@ int check_layer(const sketchssm_layer* L) {
     return SKSSM_EDIM;
   }
   if (!shape_supported(L->dk, L->dv)) return SKSSM_EDIM;
+  if (L->coef_map != SKSSM_COEF_FIXED && L->coef_map != SKSSM_COEF_STATE) return SKSSM_EFLAG;
+  if (L->coef_map == SKSSM_COEF_STATE && !(isfinite(L->coef_ridge) && L->coef_ridge > 0.f))
+    return SKSSM_EINVAL;
   if (L->window < 1 || L->window > kMaxW) return SKSSM_EDIM;
   if ((int64_t)L->batch * L->heads > INT32_MAX / 2) return SKSSM_EDIM;
   if (!L->rank_offsets_host) return SKSSM_EINVAL;
@@ -67,7 +72,9 @@ int check_buffers(const sketchssm_layer* L, const sketchssm_buffers* B, const sk
   if (nd.S && !aligned16(B->S)) return SKSSM_EINVAL;
   if (nd.U && !aligned16(B->U)) return SKSSM_EINVAL;
   if (nd.Pt && !aligned16(B->Pt)) return SKSSM_EINVAL;
-  if (nd.C && !aligned16(B->C)) return SKSSM_EINVAL;
+  const bool state_map = L->coef_map == SKSSM_COEF_STATE;
+  if (nd.C && !state_map && !aligned16(B->C)) return SKSSM_EINVAL;
+  if (nd.Cstate && state_map && !aligned16(B->Cstate)) return SKSSM_EINVAL;
   if ((nd.U || nd.Pt || nd.C) && !aligned16(B->rank_offsets)) return SKSSM_EINVAL;
   if (nd.ring) {
     if (!aligned16(B->ring_k) || !aligned16(B->ring_v) || !aligned16(B->ring_gate)) return SKSSM_EINVAL;
@@ -109,6 +116,8 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.A = B->A;
   p.err = B->err;
   p.work = B->work;
+  p.Cs = B->Cstate;
+  p.ridge = L->coef_ridge;
   if (S) {
     p.q = S->q;
     p.k = S->k;
@@ -123,11 +132,13 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
 int dispatch(const sketchssm_layer* L, int mode, const sk::Params& p, void* stream) {
   if (L->batch == 0) return SKSSM_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the state-dependent map changes only the flush and the read
+  const int coef = (L->coef_map == SKSSM_COEF_STATE && (mode == sk::MODE_FLUSH || mode == sk::MODE_READ)) ? 1 : 0;
   int rc;
   switch (L->family) {
-    case SKSSM_MAMBA2: rc = sk::launch_m2(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
-    case SKSSM_GDN: rc = sk::launch_gdn(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
-    default: rc = sk::launch_kda(mode, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+    case SKSSM_MAMBA2: rc = sk::launch_m2(mode, coef, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+    case SKSSM_GDN: rc = sk::launch_gdn(mode, coef, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
+    default: rc = sk::launch_kda(mode, coef, L->dk, L->dv, L->act_dtype, L->sketch_dtype, p, st); break;
   }
   return rc;
 }
@@ -141,7 +152,7 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{false, true, false, true, true, true, true, true, true, true};
+    const Needs nd{false, true, false, true, true, true, true, true, true, true, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_READ, make_params(layer, bufs, step), hip_stream);
   } catch (...) {
@@ -156,7 +167,7 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
     if (rc) return rc;
     if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL) return SKSSM_EFLAG;
     const bool out = step != nullptr;
-    const Needs nd{true, true, true, false, true, true, false, out, out, false};
+    const Needs nd{true, true, true, false, true, true, false, out, out, false, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     sk::Params p = make_params(layer, bufs, step);
     p.flush_all = flags == SKSSM_FLUSH_ALL;
@@ -175,7 +186,7 @@ int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* b
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{true, false, false, false, false, false, true, true, true, false};
+    const Needs nd{true, false, false, false, false, false, true, true, true, false, false};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_FULL, make_params(layer, bufs, step), hip_stream);
   } catch (...) {
@@ -188,7 +199,7 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const Needs nd{true, false, false, false, true, true, true, true, true, false};
+    const Needs nd{true, false, false, false, true, true, true, true, true, false, false};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_REPLAY, make_params(layer, bufs, step), hip_stream);
   } catch (...) {

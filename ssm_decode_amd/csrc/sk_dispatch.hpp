@@ -8,62 +8,70 @@
 namespace sk {
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
-static int launch_tile(int mode, const Params& p, hipStream_t st) {
+static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
-  constexpr size_t lds_flush = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH>::BYTES;
-  constexpr size_t lds_full = TileLds<FAM, DK, DV, WMAX, MODE_FULL>::BYTES;
-  constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY>::BYTES;
-  if (mode == MODE_FLUSH)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX>), grid, block, lds_flush, st, p);
+  constexpr size_t lds_flush = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH, 0>::BYTES;
+  constexpr size_t lds_flush_map = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH, 1>::BYTES;
+  constexpr size_t lds_full = TileLds<FAM, DK, DV, WMAX, MODE_FULL, 0>::BYTES;
+  constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY, 0>::BYTES;
+  if (mode == MODE_FLUSH && coef)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1>), grid, block, lds_flush_map, st, p);
+  else if (mode == MODE_FLUSH)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0>), grid, block, lds_flush, st, p);
   else if (mode == MODE_FULL)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX>), grid, block, lds_full, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX, 0>), grid, block, lds_full, st, p);
   else if (mode == MODE_REPLAY)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX>), grid, block, lds_replay, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX, 0>), grid, block, lds_replay, st, p);
   else
     return -4;
   return 0;
 }
 
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF>
+static void launch_read(const Params& p, hipStream_t st) {
+  if constexpr (FAM == FAM_M2) {
+    const dim3 pgrid((p.B + CQ_NB - 1) / CQ_NB, p.G, PrepGrid<COEF, DK>::ZBLOCKS + 1);
+    const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
+    hipLaunchKernelGGL((m2_prep_kernel<DK, AT, UT, WMAX, COEF>), pgrid, dim3(CQ_THREADS), 0, st, p);
+    hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, WMAX>), rgrid, dim3(64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF>), dim3(p.B * p.H), dim3(64), 0, st, p);
+  }
+}
+
 template <int FAM, int DK, int DV, typename AT, typename UT>
-static int launch_shape(int mode, const Params& p, hipStream_t st) {
+static int launch_shape(int mode, int coef, const Params& p, hipStream_t st) {
   if (p.B <= 0 || p.H <= 0) return 0;
   if (mode == MODE_READ) {
-    if (FAM == FAM_M2) {
-      const dim3 pgrid((p.B + CQ_NB - 1) / CQ_NB, p.G, CQ_ZBLOCKS + 1);
-      const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
-      if (p.W <= 16) {
-        hipLaunchKernelGGL((m2_prep_kernel<DK, AT, 16>), pgrid, dim3(CQ_THREADS), 0, st, p);
-        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 16>), rgrid, dim3(64), 0, st, p);
-      } else {
-        hipLaunchKernelGGL((m2_prep_kernel<DK, AT, 32>), pgrid, dim3(CQ_THREADS), 0, st, p);
-        hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, 32>), rgrid, dim3(64), 0, st, p);
-      }
-    } else if (p.W <= 16) {
-      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, 16>), dim3(p.B * p.H), dim3(64), 0, st, p);
+    if (p.W <= 16) {
+      if (coef) launch_read<FAM, DK, DV, AT, UT, 16, 1>(p, st);
+      else launch_read<FAM, DK, DV, AT, UT, 16, 0>(p, st);
     } else {
-      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, 32>), dim3(p.B * p.H), dim3(64), 0, st, p);
+      if (coef) launch_read<FAM, DK, DV, AT, UT, 32, 1>(p, st);
+      else launch_read<FAM, DK, DV, AT, UT, 32, 0>(p, st);
     }
   } else if (p.W <= 16) {
-    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 16>(mode, p, st)) return rc;
+    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 16>(mode, coef, p, st)) return rc;
   } else {
-    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 32>(mode, p, st)) return rc;
+    if (int rc = launch_tile<FAM, DK, DV, AT, UT, 32>(mode, coef, p, st)) return rc;
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 template <int FAM, typename AT, typename UT>
-static int launch_dtype(int mode, int dk, int dv, const Params& p, hipStream_t st) {
-  if (dk == 16 && dv == 32) return launch_shape<FAM, 16, 32, AT, UT>(mode, p, st);
-  if (dk == 64 && dv == 64) return launch_shape<FAM, 64, 64, AT, UT>(mode, p, st);
-  if (dk == 128 && dv == 64) return launch_shape<FAM, 128, 64, AT, UT>(mode, p, st);
-  if (dk == 128 && dv == 128) return launch_shape<FAM, 128, 128, AT, UT>(mode, p, st);
+static int launch_dtype(int mode, int coef, int dk, int dv, const Params& p, hipStream_t st) {
+  if (dk == 16 && dv == 32) return launch_shape<FAM, 16, 32, AT, UT>(mode, coef, p, st);
+  if (dk == 64 && dv == 64) return launch_shape<FAM, 64, 64, AT, UT>(mode, coef, p, st);
+  if (dk == 128 && dv == 64) return launch_shape<FAM, 128, 64, AT, UT>(mode, coef, p, st);
+  if (dk == 128 && dv == 128) return launch_shape<FAM, 128, 128, AT, UT>(mode, coef, p, st);
   return -2;
 }
 
 template <int FAM>
-static int launch_family(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
-  if (act == DT_F32 && sketch == DT_F32) return launch_dtype<FAM, float, float>(mode, dk, dv, p, st);
-  if (act == DT_BF16 && sketch == DT_BF16) return launch_dtype<FAM, bf16, bf16>(mode, dk, dv, p, st);
+static int launch_family(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p,
+                         hipStream_t st) {
+  if (act == DT_F32 && sketch == DT_F32) return launch_dtype<FAM, float, float>(mode, coef, dk, dv, p, st);
+  if (act == DT_BF16 && sketch == DT_BF16) return launch_dtype<FAM, bf16, bf16>(mode, coef, dk, dv, p, st);
   return -3;
 }
 

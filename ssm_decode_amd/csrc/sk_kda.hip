@@ -3,7 +3,7 @@
 #include "sk_dispatch.hpp"
 
 namespace sk {
-int launch_kda(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
-  return launch_family<FAM_KDA>(mode, dk, dv, act, sketch, p, st);
+int launch_kda(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
+  return launch_family<FAM_KDA>(mode, coef, dk, dv, act, sketch, p, st);
 }
 }  // namespace sk

@@ -3,7 +3,7 @@
 #include "sk_dispatch.hpp"
 
 namespace sk {
-int launch_m2(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
-  return launch_family<FAM_M2>(mode, dk, dv, act, sketch, p, st);
+int launch_m2(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st) {
+  return launch_family<FAM_M2>(mode, coef, dk, dv, act, sketch, p, st);
 }
 }  // namespace sk

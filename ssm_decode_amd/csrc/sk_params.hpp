@@ -27,6 +27,8 @@ struct Params {
   const float* A;
   int32_t* err;
   void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
+  void* Cs;             // state-dependent coefficient maps [B][R][dk] sketch dtype
+  float ridge;          // relative ridge of the state-dependent map
   const void* q;
   const void* k;
   const void* v;
@@ -49,8 +51,9 @@ struct M2Work {
 
 // Launch one kernel of `family` for `mode`; returns 0, or -2 when the shape
 // / dtype combination has no instantiation, or -5 on a launch error.
-int launch_m2(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
-int launch_gdn(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
-int launch_kda(int mode, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+// coef: 0 the fixed per-head map, 1 the state-dependent map.
+int launch_m2(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+int launch_gdn(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
+int launch_kda(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p, hipStream_t st);
 
 }  // namespace sk

@@ -1,7 +1,11 @@
 // Non-flush sketched-read kernels.  They never touch the state S: each step
-// reads the sketch U, the buffered ring entries and the fixed coefficient
-// map C, appends the step's entry to the ring and advances the ring count.
+// reads the sketch U, the buffered ring entries and the coefficient map C
+// (the fixed per-head table, or each tile's state-dependent map as its last
+// flush wrote it), appends the step's entry to the ring and advances the
+// ring count.
 #pragma once
+
+#include <type_traits>
 
 #include "sk_device.hpp"
 #include "sk_params.hpp"
@@ -28,9 +32,16 @@ namespace sk {
 constexpr int M2R_MAXHPG = 16;     // heads per B/C group (at most)
 constexpr int CQ_NB = 8;           // sequences per prep workgroup
 constexpr int CQ_THREADS = 256;
-constexpr int CQ_LPR = 4;          // lanes per coefficient row
-constexpr int CQ_ROWS = CQ_THREADS / CQ_LPR;
-constexpr int CQ_ZBLOCKS = (M2R_MAXHPG * 16 + CQ_ROWS - 1) / CQ_ROWS;
+// Coefficient rows of a prep workgroup: the fixed map keeps a row's C
+// segment in registers across the CQ_NB sequences (4 lanes a row); the
+// state-dependent map has a row per sequence, read once (8 lanes a row keep
+// the CQ_NB rows' segments in registers at dk >= 64).
+template <int COEF, int DK>
+struct PrepGrid {
+  static constexpr int LPR = COEF && DK >= 64 ? 8 : 4;     // lanes per coefficient row
+  static constexpr int ROWS = CQ_THREADS / LPR;            // rows per workgroup
+  static constexpr int ZBLOCKS = (M2R_MAXHPG * 16 + ROWS - 1) / ROWS;
+};
 constexpr int DOT_LPP = 4;         // lanes per (sequence, slot) dot product
 
 template <int DK, typename AT, int WMAX>
@@ -101,9 +112,11 @@ __device__ __forceinline__ void m2_prep_dots(const Params& p) {
   }
 }
 
-template <int DK, typename AT, int WMAX>
+template <int DK, typename AT, typename UT, int WMAX, int COEF>
 __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
-  if (blockIdx.z == CQ_ZBLOCKS) {                  // uniform: the dot-product block
+  using PG = PrepGrid<COEF, DK>;
+  constexpr int CQ_LPR = PG::LPR, CQ_ROWS = PG::ROWS;
+  if (blockIdx.z == PG::ZBLOCKS) {                 // uniform: the dot-product block
     m2_prep_dots<DK, AT, WMAX>(p);
     return;
   }
@@ -122,12 +135,19 @@ __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
   const int nb = min(CQ_NB, p.B - b0);
   const int row = rb + tid / CQ_LPR;
   const int qt = tid & (CQ_LPR - 1);
-  float c[SEGC];
-  if (row < rows) {
-    ldn<SEGC>(p.C + (size_t)(roff0 + row) * DK + qt * SEGC, c);
-  } else {
+  // C rows: the fixed map's row once for every sequence, or the row of each
+  // sequence's own map
+  constexpr int NCR = COEF ? CQ_NB : 1;
+  VecN<typename std::conditional<COEF != 0, UT, float>::type, SEGC> c[NCR];
 #pragma unroll
-    for (int e = 0; e < SEGC; ++e) c[e] = 0.f;
+  for (int bb = 0; bb < NCR; ++bb) {
+    const int rr = row < rows ? row : 0;          // clamped: loads stay unconditional
+    if constexpr (COEF) {
+      const int b = b0 + (bb < nb ? bb : 0);
+      c[bb] = ldraw<SEGC>(reinterpret_cast<const UT*>(p.Cs) + ((size_t)b * p.R + roff0 + rr) * DK + qt * SEGC);
+    } else {
+      c[bb] = ldraw<SEGC>(p.C + (size_t)(roff0 + rr) * DK + qt * SEGC);
+    }
   }
   const AT* q = reinterpret_cast<const AT*>(p.q);
   float qv[QIT][4];
@@ -148,15 +168,16 @@ __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
 #pragma unroll
   for (int bb = 0; bb < CQ_NB; ++bb) {
     if (bb < nb) {
+      const auto& cr = c[COEF ? bb : 0];
       const float* qs = &s_q[bb][qt * SEGC];
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
       for (int e = 0; e < SEGC; e += 4) {
         const float4 qq = *reinterpret_cast<const float4*>(qs + e);
-        a0 += c[e] * qq.x;
-        a1 += c[e + 1] * qq.y;
-        a2 += c[e + 2] * qq.z;
-        a3 += c[e + 3] * qq.w;
+        a0 += vget(cr, e) * qq.x;
+        a1 += vget(cr, e + 1) * qq.y;
+        a2 += vget(cr, e + 2) * qq.z;
+        a3 += vget(cr, e + 3) * qq.w;
       }
       const float acc = xsum<0, ilog2c(CQ_LPR)>((a0 + a1) + (a2 + a3));
       if (qt == 0 && row < rows) cq[(size_t)(b0 + bb) * p.R + roff0 + row] = acc;
@@ -348,7 +369,7 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
 // EK l .. EK l + EK - 1 of r and k_i and the output columns EV l .. ; the
 // per-slot scalars of slot i sit in lane i and are read with readlane.  The
 // append stores the step's entry from the registers that hold it.
-template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF>
 __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
   constexpr int EK = DK >= 64 ? DK / 64 : 1;
   constexpr int EV = DV >= 64 ? DV / 64 : 1;
@@ -415,9 +436,13 @@ __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
     const float al_l = FAM == FAM_GDN ? ring_g[ls] : 1.f;
     const float be_l = ring_b[ls];
     float cr[16][EK];
+    const UT* Csb = reinterpret_cast<const UT*>(p.Cs) + ((size_t)b * p.R + off) * DK + lk;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < rk) ldn<EK>(p.C + (size_t)(off + j) * DK + lk, cr[j]);
+      if (j < rk) {
+        if constexpr (COEF) ldn<EK>(Csb + (size_t)j * DK, cr[j]);
+        else ldn<EK>(p.C + (size_t)(off + j) * DK + lk, cr[j]);
+      }
     VecN<UT, EV> us[16];
     const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + lv;
 #pragma unroll

@@ -54,7 +54,7 @@ struct TileShape {
 };
 
 // LDS layout of a tile kernel (offsets in floats).
-template <int FAM, int DK, int DV, int WMAX, int MODE>
+template <int FAM, int DK, int DV, int WMAX, int MODE, int COEF>
 struct TileLds {
   using T = TileShape<DK, DV>;
   static constexpr int KWS = WMAX + 4;                         // Mamba-2 key row stride ([m][slot])
@@ -80,7 +80,19 @@ struct TileLds {
   static constexpr bool CHUNK = FAM != FAM_M2 && MODE == MODE_FLUSH;
   static constexpr int DN_END = CHUNK ? GF + DK : 0;
   static constexpr int T0 = KEYS0 + (KEYS > BASIS ? KEYS : BASIS);
-  static constexpr int TOTAL = T0 > DN_END ? T0 : DN_END;
+  // state-dependent map (flush): each wave stages 16 state rows of its
+  // column block below the basis while the sketch is formed; once every wave
+  // is past the sketch, the partial Y blocks and Gram matrix of every wave
+  // ([wave][MB + 1][lane] of 4 floats) and the 16 x 16 inverse reuse the
+  // whole area
+  static constexpr int SSTR = T::CB + 4;                       // staged row stride
+  static constexpr int SST = 0;
+  static constexpr int PART = 0;
+  static constexpr int GINV = PART + T::NCB * (T::MB + 1) * 256;
+  static constexpr int MAP_END = COEF ? GINV + 256 : 0;
+  static_assert(!COEF || T::NCB * 16 * SSTR <= KEYS0, "staged state rows overlap the basis");
+  static constexpr int T1 = T0 > DN_END ? T0 : DN_END;
+  static constexpr int TOTAL = T1 > MAP_END ? T1 : MAP_END;
   static constexpr int BYTES = TOTAL * 4;
   static_assert(V % 4 == 0 && KEYS0 % 4 == 0 && P0 % 4 == 0 && GF % 4 == 0,
                 "LDS regions must be 16-byte aligned");
@@ -114,13 +126,158 @@ __device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, d, 0, 0, 0);
 }
 
+// State-dependent coefficient map of one tile at the flush (project page,
+// per-window flush panel: C = (U^T U)^+ U^T S0^T; paper App. A.2.1-A.2.2):
+// with U_h the sketch rows as stored (rounded to the sketch dtype) and S the
+// updated state,
+//     G = U_h U_h^T (r x r),  Y = U_h S^T (r x dk),  C = (G + lambda I)^{-1} Y,
+//     lambda = ridge * trace(G) / r   (C = 0 when the sketch is zero),
+// stored in the sketch dtype as rows off .. off + r - 1 of sequence b.
+//
+// Both contractions run over the state's columns, which the register layout
+// spreads over lanes (it contracts over rows only), so:
+//   - the sketch values a lane already holds, u_j (j = lane % 16) at the 8
+//     columns 8 (lane / 16) + t of its wave's block, are the A operand of
+//     v_mfma_f32_16x16x4_f32 for K-step t; for G they are the B operand too;
+//   - for Y each wave stages its 16 x 32 block of every 16-row band of S in
+//     LDS and reads it back transposed as the B operand (8 K-steps a band);
+//   - the waves' partial G and Y blocks are summed through LDS; wave 0
+//     inverts G + lambda I (Gauss-Jordan, no pivoting: the matrix is
+//     symmetric positive definite) with lane (j, i / 4) holding column j;
+//   - C = (G + lambda I)^{-1} Y is one more 4-step MFMA per 16-column band,
+//     each wave taking the bands b % waves == its index.
+// Padding rows j >= r of the sketch are zero, so the padded part of G is set
+// to the identity and the padded rows of C are zero and not stored.
+template <int DK, int DV, typename UT, typename LY>
+__device__ __forceinline__ void coef_map(const Params& p, float* smem,
+                                         const f32x4v (&sacc)[DK / 16][TileShape<DK, DV>::NCC],
+                                         const f32x4v (&u)[TileShape<DK, DV>::NCC], int b, int off,
+                                         int r) {
+  using T = TileShape<DK, DV>;
+  constexpr int NCC = T::NCC, MB = T::MB, NCB = T::NCB, SSTR = LY::SSTR;
+  static_assert(NCC == 2, "the map assumes two columns per lane (8 sketch columns per lane)");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int cg = lane & 15, rg = lane >> 4;
+
+  // the sketch as stored: uh[t] = u_j at column 8 rg + t of the wave's block
+  float uh[8];
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+    for (int c = 0; c < NCC; ++c) uh[NCC * vv + c] = to_f32(Store<UT>::cvt(u[c][vv]));
+
+  f32x4v gp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) gp = mfma16x4(uh[t], uh[t], gp);
+
+  // Y blocks: band mb gives Y[4 rg + v][16 mb + cg] in lane (cg, rg)
+  float* s_st = smem + LY::SST + wv * 16 * SSTR;
+  f32x4v yp[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *reinterpret_cast<float2*>(s_st + (4 * rg + v) * SSTR + NCC * cg) =
+          make_float2(sacc[mb][0][v], sacc[mb][1][v]);
+    // read back by the same wave (its LDS operations complete in order):
+    // row 16 mb + cg, columns 8 rg .. 8 rg + 7 of the block
+    const float4 s0 = *reinterpret_cast<const float4*>(s_st + cg * SSTR + 8 * rg);
+    const float4 s1 = *reinterpret_cast<const float4*>(s_st + cg * SSTR + 8 * rg + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    yp[mb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) yp[mb] = mfma16x4(uh[t], sv[t], yp[mb]);
+  }
+
+  __syncthreads();          // every wave is past its sketch and its staging
+  f32x4v* part = reinterpret_cast<f32x4v*>(smem + LY::PART);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) part[(wv * (MB + 1) + mb) * 64 + lane] = yp[mb];
+  part[(wv * (MB + 1) + MB) * 64 + lane] = gp;
+  __syncthreads();
+
+  float* s_gi = smem + LY::GINV;
+  if (wv == 0) {
+    f32x4v g = part[MB * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NCB; ++w) g += part[(w * (MB + 1) + MB) * 64 + lane];
+    // lane (cg, rg) holds G[4 rg + v][cg]
+    float dg = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (4 * rg + v == cg && cg < r) dg += g[v];
+    const float tr = wave_sum(dg);
+    const float lam = tr > 0.f ? p.ridge * tr / (float)r : 1.f;
+    float m[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * rg + v;
+      const bool in = i < r && cg < r;
+      m[v] = (i == cg) ? (in ? g[v] + lam : 1.f) : (in ? g[v] : 0.f);
+    }
+    // in-place Gauss-Jordan inversion, pivot k: with p = 1 / M[k][k],
+    //   M[k][k] <- p,            M[k][j] <- M[k][j] p              (j != k)
+    //   M[i][k] <- -M[i][k] p,   M[i][j] <- M[i][j] - M[i][k] M[k][j] p
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float mkj = __shfl(m[k & 3], (k >> 2) * 16 + cg);     // M[k][cg]
+      float mik[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mik[v] = __shfl(m[v], rg * 16 + k);   // M[4 rg + v][k]
+      const float piv = 1.f / lane_value(mkj, k);                // lane k holds M[k][k]
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 4 * rg + v;
+        if (i == k) m[v] = (cg == k) ? piv : mkj * piv;
+        else m[v] = (cg == k) ? -mik[v] * piv : m[v] - mik[v] * (mkj * piv);
+      }
+    }
+    // inverse row-major: s_gi[i][j]
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_gi[(4 * rg + v) * 16 + cg] = m[v];
+  }
+  // each wave's own bands: sum the partial Y blocks
+  constexpr int MBW = (MB + NCB - 1) / NCB;
+  f32x4v y[MBW];
+#pragma unroll
+  for (int q = 0; q < MBW; ++q) {
+    const int mb = wv + q * NCB;
+    y[q] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    if (mb < MB) {
+#pragma unroll
+      for (int w = 0; w < NCB; ++w) y[q] += part[(w * (MB + 1) + mb) * 64 + lane];
+    }
+  }
+  __syncthreads();
+  // A operand of step v: Ginv[cg][4 rg + v]
+  const float4 ga4 = *reinterpret_cast<const float4*>(s_gi + cg * 16 + 4 * rg);
+  const float ga[4] = {ga4.x, ga4.y, ga4.z, ga4.w};
+  UT* Cb = reinterpret_cast<UT*>(p.Cs) + ((size_t)b * p.R + off) * DK;
+#pragma unroll
+  for (int q = 0; q < MBW; ++q) {
+    const int mb = wv + q * NCB;
+    if (mb < MB) {
+      f32x4v cm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cm = mfma16x4(ga[v], y[q][v], cm);
+      // lane holds C[4 rg + v][16 mb + cg]
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 4 * rg + v;
+        if (j < r) st(Cb + (size_t)j * DK + 16 * mb + cg, cm[v]);
+      }
+    }
+  }
+}
+
 // (the delta-rule flush runs three waves per SIMD: its chunked update has
 // serial phases that more resident tiles hide)
-template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX>
+template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX, int COEF>
 __global__ void __launch_bounds__((TileShape<DK, DV>::THREADS), (MODE == MODE_FLUSH && FAM != FAM_M2 ? 3 : 2))
 tile_kernel(Params p) {
   using T = TileShape<DK, DV>;
-  using LY = TileLds<FAM, DK, DV, WMAX, MODE>;
+  using LY = TileLds<FAM, DK, DV, WMAX, MODE, COEF>;
   constexpr int CB = T::CB, NCC = T::NCC, MB = T::MB, PS = T::PS;
   constexpr int NT = T::THREADS;
   constexpr int KWS = LY::KWS;
@@ -776,6 +933,7 @@ tile_kernel(Params p) {
           stn<8>(Ub, x);
         }
       }
+      if constexpr (COEF) coef_map<DK, DV, UT, LY>(p, smem, sacc, u, b, off, r);
     }
   }
 

@@ -40,18 +40,24 @@ class DeviceStep:
                                   _ptr(self.beta), _ptr(self.o))
 
 
+COEF = {"fixed": abi.SKSSM_COEF_FIXED, "state": abi.SKSSM_COEF_STATE}
+
+
 class DecodeLayer:
     """All persistent buffers of one layer: S, U, Pt, C, rank offsets, the
     ring (k, v, gate, beta), the per-tile ring counts, A, the error word and
-    the read's workspace."""
+    the read's workspace.  coef = "fixed" reads the per-head map Cmap;
+    coef = "state" has every flush write each tile's own map into Cstate
+    ([B][R][dk], sketch dtype) with the relative ridge ``ridge``."""
 
     def __init__(self, family: str, batch: int, heads: int, qk_groups: int, dk: int, dv: int,
                  window: int, act: str, sketch: str, rank_offsets: np.ndarray,
-                 device: str = "cuda"):
+                 device: str = "cuda", coef: str = "fixed", ridge: float = 1e-4):
         self.family, self.B, self.H, self.G = family, batch, heads, qk_groups
         self.dk, self.dv, self.W = dk, dv, window
         self.act, self.sketch = act, sketch
         self.device = device
+        self.coef, self.ridge = coef, float(ridge)
         self.offsets_host = np.ascontiguousarray(np.asarray(rank_offsets, dtype=np.int32))
         self.R = int(self.offsets_host[-1])
         at, ut = TORCH_DTYPE[act], TORCH_DTYPE[sketch]
@@ -61,6 +67,7 @@ class DecodeLayer:
         self.U = z((B, self.R, dv), ut)
         self.Pt = z((self.R, dk), torch.float32)
         self.Cmap = z((self.R, dk), torch.float32)
+        self.Cstate = z((B, self.R, dk), ut) if coef == "state" else None
         self.offsets = torch.from_numpy(self.offsets_host.copy()).to(device)
         self.ring_k = z((B, G, W, dk), at)
         self.ring_v = z((B, H, W, dv), at)
@@ -80,7 +87,8 @@ class DecodeLayer:
         self.err = z((4,), torch.int32)
         self._layer = abi.sketchssm_layer(
             FAMILY[family], B, H, G, dk, dv, W, DTYPE[act], DTYPE[sketch],
-            self.offsets_host.ctypes.data_as(C.POINTER(C.c_int32)))
+            self.offsets_host.ctypes.data_as(C.POINTER(C.c_int32)), COEF[coef],
+            self.ridge if coef == "state" else 0.0)
         nwork = abi.sketchssm_workspace_bytes(self._layer)
         if nwork < 0:
             raise ValueError(f"invalid layer description (code {nwork})")
@@ -88,7 +96,7 @@ class DecodeLayer:
         self._bufs = abi.sketchssm_buffers(
             _ptr(self.S), _ptr(self.U), _ptr(self.Pt), _ptr(self.Cmap), _ptr(self.offsets),
             _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_gate), _ptr(self.ring_beta),
-            _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work))
+            _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work), _ptr(self.Cstate))
 
     # -------------------------------------------------------------- structs
     @property

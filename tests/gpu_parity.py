@@ -41,6 +41,7 @@ class ParityReport:
     max_o: float = 0.0
     max_S: float = 0.0
     max_U: float = 0.0
+    max_C: float = 0.0
     flushes: int = 0
     count_mismatch: int = 0
     err_word: int = 0
@@ -49,7 +50,7 @@ class ParityReport:
 
     def line(self) -> str:
         return (f"{self.name} {self.method}: steps={self.steps} tiles={self.tiles} "
-                f"max rel-L2 o={self.max_o:.3e} S={self.max_S:.3e} U={self.max_U:.3e} "
+                f"max rel-L2 o={self.max_o:.3e} S={self.max_S:.3e} U={self.max_U:.3e} C={self.max_C:.3e} "
                 f"flush-steps={self.flushes} count-mismatch={self.count_mismatch} "
                 f"err={self.err_word} ({self.seconds:.1f}s)")
 
@@ -68,7 +69,11 @@ def all_tiles(cfg) -> np.ndarray:
 
 
 def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray = None,
-               numpy_all: bool = True, li: synth.LayerInputs = None, log=True) -> ParityReport:
+               numpy_all: bool = True, li: synth.LayerInputs = None, log=True,
+               coef: str = "fixed", ridge: float = 1e-4) -> ParityReport:
+    """coef = "state": the flush forms each tile's own coefficient map with the
+    relative ridge ``ridge`` (both sides use its fp32 value) and the maps of
+    the flushed tiles are compared too."""
     t0 = time.time()
     steps = cfg.steps if steps is None else steps
     li = synth.make_layer_inputs(cfg) if li is None else li
@@ -79,14 +84,15 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     W = cfg.window
 
     # --- HIP side
-    lay = feed.make_layer(cfg, li)
+    lay = feed.make_layer(cfg, li, coef=coef, ridge=ridge)
     feed.fill_state(lay, cfg, exact_seqs=seqs, numpy_all=numpy_all)
     # --- oracle side
     S0s = synth.initial_state(cfg, b_idx=seqs)
     S0_t = S0s[seq_rows[tiles[:, 0]], tiles[:, 1]]
     orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, W, li.ranks, li.offsets, li.Pt, li.C, li.A,
                              tiles, S0_t, cfg.heads, cfg.qk_groups, state_store="f32",
-                             sketch_store=cfg.sketch, out_store=cfg.act)
+                             sketch_store=cfg.sketch, out_store=cfg.act, coef=coef,
+                             ridge=float(np.float32(ridge)))
     count0_t = li.count0[tiles[:, 0], tiles[:, 1]]
     if method == "sketch":
         assert feed.prime(lay, li) == 0
@@ -96,7 +102,21 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
         lay.count.copy_(torch.from_numpy(li.count0).to(lay.device))
     orc.count[:] = count0_t if method != "standard" else 0
 
-    rep = ParityReport(cfg.name, method, steps, len(tiles))
+    rep = ParityReport(cfg.name, method + ("" if coef == "fixed" else "/state-map"), steps, len(tiles))
+
+    def compare_maps(sel):
+        C_gpu = lay.Cstate[tiles[sel, 0]].float().cpu().numpy().astype(np.float64)
+        Cg, Co = [], []
+        for i, ti in enumerate(sel):
+            h = tiles[ti, 1]
+            off, r = li.offsets[h], li.ranks[h]
+            Cg.append(C_gpu[i, off:off + r])
+            Co.append(orc.C[ti, :r])
+        rep.max_C = max(rep.max_C, rel_l2(np.concatenate(Cg), np.concatenate(Co)))
+
+    if method == "sketch" and coef == "state":
+        torch.cuda.synchronize()
+        compare_maps(np.arange(len(tiles)))
     step = lay.new_step()
     tb = torch.from_numpy(tiles[:, 0]).to(lay.device)
     th = torch.from_numpy(tiles[:, 1]).to(lay.device)
@@ -152,15 +172,18 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
                     Ug.append(U_gpu[i, off:off + r])
                     Uo.append(orc.U[ti, :r])
                 rep.max_U = max(rep.max_U, rel_l2(np.concatenate(Ug), np.concatenate(Uo)))
+                if coef == "state":
+                    compare_maps(sel)
         if log and (t % 16 == 15 or t == steps - 1):
-            print(f"  [{cfg.name} {method}] step {t + 1}/{steps} max o={rep.max_o:.2e} "
-                  f"S={rep.max_S:.2e} U={rep.max_U:.2e}", flush=True)
+            print(f"  [{cfg.name} {rep.method}] step {t + 1}/{steps} max o={rep.max_o:.2e} "
+                  f"S={rep.max_S:.2e} U={rep.max_U:.2e} C={rep.max_C:.2e}", flush=True)
         assert e <= t_o, f"{cfg.name} {method} step {t}: rel-L2(o) = {e:.3e} > {t_o}"
     rep.err_word = lay.error_word()
     rep.seconds = time.time() - t0
     assert rep.count_mismatch == 0, rep.line()
     assert rep.max_S <= TOL_F32, rep.line()
     assert rep.max_U <= t_s, rep.line()
+    assert rep.max_C <= t_s, rep.line()
     assert rep.err_word == 0, rep.line()
     if log:
         print("  " + rep.line(), flush=True)

@@ -46,17 +46,17 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launc
 
 
 def _layer(offsets, family=abi.SKSSM_MAMBA2, batch=2, heads=4, groups=4, dk=16, dv=32, W=4,
-           act=abi.SKSSM_F32, sk=abi.SKSSM_F32):
+           act=abi.SKSSM_F32, sk=abi.SKSSM_F32, coef=abi.SKSSM_COEF_FIXED, ridge=0.0):
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
     L = abi.sketchssm_layer(family, batch, heads, groups, dk, dv, W, act, sk,
-                            off.ctypes.data_as(C.POINTER(C.c_int32)))
+                            off.ctypes.data_as(C.POINTER(C.c_int32)), coef, ridge)
     L._keep = off
     return L
 
 
 def _bufs(**over):
     f = dict(S=FAKE, U=FAKE, Pt=FAKE, C=FAKE, rank_offsets=FAKE, ring_k=FAKE, ring_v=FAKE,
-             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE)
+             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE, Cstate=FAKE)
     f.update(over)
     return abi.sketchssm_buffers(**f)
 
@@ -170,3 +170,26 @@ def test_read_needs_its_workspace(lib):
     Lg = _layer(OK_OFF, family=abi.SKSSM_GDN, batch=0)
     assert abi.sketchssm_read(Lg, _bufs(work=None), _step()) == 0
     assert abi.sketchssm_read(_layer(OK_OFF, batch=0), _bufs(work=None), _step()) == 0
+
+
+def test_coefficient_map_mode(lib):
+    """The map mode is a flag (unknown values: EFLAG); the state-dependent map
+    needs a finite positive ridge and Cstate for the read and the flush, and
+    no fixed table C; the fixed map never looks at Cstate."""
+    for bad in (2, -1):
+        L = _layer(OK_OFF, coef=bad, ridge=1e-4)
+        assert _all_calls(L, _bufs(), _step()) == [abi.SKSSM_EFLAG] * 4
+    for ridge in (0.0, -1e-3, float("nan"), float("inf")):
+        L = _layer(OK_OFF, coef=abi.SKSSM_COEF_STATE, ridge=ridge)
+        assert _all_calls(L, _bufs(), _step()) == [abi.SKSSM_EINVAL] * 4
+    L = _layer(OK_OFF, coef=abi.SKSSM_COEF_STATE, ridge=1e-4)
+    for cs in (None, FAKE + 8):
+        assert abi.sketchssm_read(L, _bufs(Cstate=cs), _step()) == abi.SKSSM_EINVAL
+        assert abi.sketchssm_flush(L, _bufs(Cstate=cs), None, abi.SKSSM_FLUSH_ALL) == abi.SKSSM_EINVAL
+    L0 = _layer(OK_OFF, coef=abi.SKSSM_COEF_STATE, ridge=1e-4, batch=0)
+    assert _all_calls(L0, _bufs(C=None), _step()) == [0] * 4
+    assert abi.sketchssm_full_step(L0, _bufs(Cstate=None), _step()) == 0
+    assert abi.sketchssm_replay_step(L0, _bufs(Cstate=None), _step()) == 0
+    Lf = _layer(OK_OFF, batch=0)
+    assert _all_calls(Lf, _bufs(Cstate=None), _step()) == [0] * 4
+    assert abi.sketchssm_read(_layer(OK_OFF), _bufs(C=None), _step()) == abi.SKSSM_EINVAL
