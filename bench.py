@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=16, help="device-resident step inputs cycled")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-baselines", action="store_true", help="skip full/replay GPU baselines")
+    ap.add_argument("--no-state-map", action="store_true",
+                    help="skip the run with the state-dependent coefficient map")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
     ap.add_argument("--cpu-windows", type=int, default=16, help="windows in the CPU sample")
     return ap.parse_args()
@@ -80,30 +82,32 @@ def main():
     L = args.layers or int(np.clip(np.ceil(2 * 256 * 2 ** 20 / nonflush), 2, 8))
     log(f"[bench] {cfg.name}: B={cfg.batch} H={cfg.heads} dk={cfg.dk} dv={cfg.dv} W={W} "
         f"R={int(li.offsets[-1])} layers={L} (sketch+ring {nonflush / 1e6:.0f} MB each)")
-    layers = []
-    for l in range(L):
-        lay = first if l == 0 else feed.make_layer(cfg, li, device=dev)
-        if l == 0:
-            feed.fill_state(lay, cfg, numpy_all=False)
-        else:
-            lay.S.copy_(layers[0].S)
-        assert feed.prime(lay, li) == 0
-        layers.append(lay)
-    torch.cuda.synchronize()
-    log(f"[bench] layers ready ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
+    feed.fill_state(first, cfg, numpy_all=False)
+    S_init = first.S.clone()
+
+    def make_layers(coef):
+        out = []
+        for _ in range(L):
+            lay = feed.make_layer(cfg, li, device=dev, coef=coef)
+            lay.S.copy_(S_init)
+            assert feed.prime(lay, li) == 0
+            out.append(lay)
+        torch.cuda.synchronize()
+        return out
 
     # -------------------------------------------------- step input pool
     P = max(1, args.pool)
     pool = []
     for t in range(P):
-        st = layers[0].new_step()
+        st = first.new_step()
         q, k, v, gate, beta = torch_gen.step_inputs(cfg, t, dev)
         st.q.copy_(q); st.k.copy_(k); st.v.copy_(v); st.gate.copy_(gate)
         if beta is not None:
             st.beta.copy_(beta)
         pool.append(st)
     # one output buffer per layer
-    outs = [layers[0].new_step().o for _ in range(L)]
+    outs = [first.new_step().o for _ in range(L)]
+    del first
     steps_structs = []
     for t in range(P):
         row = []
@@ -117,84 +121,91 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     phase = int(li.phase[0])
     ragged = cfg.ragged
-
-    def one_step(t, ev=None, stream_handle=None):
-        sh_ = sh if stream_handle is None else stream_handle
-        due = ragged or ((t - phase) % W == 0)
-        for l, lay in enumerate(layers):
-            st = steps_structs[t % P][l]
-            if ev is not None:
-                ev["read"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-                ev["read"][-1][0].record(stream)
-            rc = abi.sketchssm_read(lay.layer_struct, lay.buffers_struct, st, sh_)
-            if ev is not None:
-                ev["read"][-1][1].record(stream)
-            assert rc == 0
-            if due:
-                if ev is not None:
-                    ev["flush"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-                    ev["flush"][-1][0].record(stream)
-                rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
-                                         abi.SKSSM_FLUSH_DUE, sh_)
-                if ev is not None:
-                    ev["flush"][-1][1].record(stream)
-                assert rc == 0
-
-    # the timed region starts at a window boundary
-    t = 0
-    for _ in range(args.warmup):
-        one_step(t)
-        t += 1
-    while (t - phase - 1) % W != 0 and not ragged:
-        one_step(t)
-        t += 1
-    torch.cuda.synchronize()
-
-    # ---- per-kernel durations: eager launches bracketed by HIP events on
-    # the launch stream, over two windows
-    ev = {"read": [], "flush": []}
-    for i in range(2 * W):
-        one_step(t + i, ev)
-    torch.cuda.synchronize()
-    t += 2 * W
-    read_us = [a.elapsed_time(b) * 1000 for a, b in ev["read"]]
-    flush_us = [a.elapsed_time(b) * 1000 for a, b in ev["flush"]]
-    flush_avg = float(np.mean(flush_us)) if flush_us else float("nan")
-    read_avg = float(np.mean(read_us))
-
-    # ---- the timed steps: exactly K steps (every layer's read, and its flush
-    # when a window closes) captured in one HIP graph and replayed once, so
-    # that host launch overhead is not timed; the device ring counts advance
-    # exactly as in eager execution
     K = args.steps
 
-    def realign():
-        nonlocal t
-        while (t - phase - 1) % W != 0 and not ragged:
+    def measure(layers):
+        """Event-timed eager kernels over two windows, then exactly K steps
+        captured in one HIP graph and timed around its replay."""
+
+        def one_step(t, ev=None, stream_handle=None):
+            sh_ = sh if stream_handle is None else stream_handle
+            due = ragged or ((t - phase) % W == 0)
+            for l, lay in enumerate(layers):
+                st = steps_structs[t % P][l]
+                if ev is not None:
+                    ev["read"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                    ev["read"][-1][0].record(stream)
+                rc = abi.sketchssm_read(lay.layer_struct, lay.buffers_struct, st, sh_)
+                if ev is not None:
+                    ev["read"][-1][1].record(stream)
+                assert rc == 0
+                if due:
+                    if ev is not None:
+                        ev["flush"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        ev["flush"][-1][0].record(stream)
+                    rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
+                                             abi.SKSSM_FLUSH_DUE, sh_)
+                    if ev is not None:
+                        ev["flush"][-1][1].record(stream)
+                    assert rc == 0
+
+        def realign(t):
+            while (t - phase - 1) % W != 0 and not ragged:
+                one_step(t)
+                t += 1
+            return t
+
+        # the timed region starts at a window boundary
+        t = 0
+        for _ in range(args.warmup):
             one_step(t)
             t += 1
+        t = realign(t)
+        torch.cuda.synchronize()
 
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        capture_handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for i in range(K):
-            one_step(t + i, stream_handle=capture_handle)
-    torch.cuda.synchronize()
-    graph.replay()                      # warm replay
-    torch.cuda.synchronize()
-    t += K
-    realign()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    graph.replay()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    t += K
-    total_ms = start.elapsed_time(stop)
-    us_per_step = total_ms * 1000.0 / (K * L)
-    err = max(lay.error_word() for lay in layers)
-    assert err == 0, f"device error word {err}"
+        # per-kernel durations: eager launches bracketed by HIP events on
+        # the launch stream, over two windows
+        ev = {"read": [], "flush": []}
+        for i in range(2 * W):
+            one_step(t + i, ev)
+        torch.cuda.synchronize()
+        t += 2 * W
+        read_us = [a.elapsed_time(b) * 1000 for a, b in ev["read"]]
+        flush_us = [a.elapsed_time(b) * 1000 for a, b in ev["flush"]]
+
+        # the timed steps: exactly K steps (every layer's read, and its flush
+        # when a window closes) captured in one HIP graph and replayed once,
+        # so that host launch overhead is not timed; the device ring counts
+        # advance exactly as in eager execution
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            capture_handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(K):
+                one_step(t + i, stream_handle=capture_handle)
+        torch.cuda.synchronize()
+        graph.replay()                      # warm replay
+        torch.cuda.synchronize()
+        t += K
+        t = realign(t)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        graph.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        del graph
+        err = max(lay.error_word() for lay in layers)
+        assert err == 0, f"device error word {err}"
+        return {"us_per_step": total_ms * 1000.0 / (K * L),
+                "flush_avg": float(np.mean(flush_us)) if flush_us else float("nan"),
+                "flush_n": len(flush_us), "read_avg": float(np.mean(read_us)), "read_n": len(read_us)}
+
+    layers = make_layers("fixed")
+    log(f"[bench] layers ready ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
+    m = measure(layers)
+    us_per_step, flush_avg, read_avg = m["us_per_step"], m["flush_avg"], m["read_avg"]
+    flush_us, read_us = [0] * m["flush_n"], [0] * m["read_n"]
     log(f"[bench] sketch: {us_per_step:.2f} us/step/layer (graph of {K} steps x {L} layers); "
         f"flush avg {flush_avg:.1f} us ({len(flush_us)} launches); read avg {read_avg:.2f} us")
 
@@ -245,6 +256,37 @@ def main():
     if not args.no_baselines:
         approx = sketch_error(cfg, li, layers[0], pool, steps=2 * W)
         log(f"[bench] sketched vs exact read: {approx}")
+
+    # --------------- the state-dependent coefficient map (same workload)
+    state_map = None
+    if not args.no_state_map:
+        sm = {}
+        if not args.no_baselines:
+            sm["sketch_error"] = sketch_error(cfg, li, layers[0], pool, steps=2 * W, coef="state")
+            log(f"[bench] state-map sketched vs exact read: {sm['sketch_error']}")
+        del layers
+        torch.cuda.empty_cache()
+        layers = make_layers("state")
+        ms = measure(layers)
+        lbs = traffic.config_bytes(cfg, int(li.offsets[-1]), "state")
+        sgbs = lbs.flush_launch / (ms["flush_avg"] * 1e-6) / 1e9
+        sm.update({
+            "us_per_step": round(ms["us_per_step"], 3),
+            "algorithmic_bytes_per_step": int(round(lbs.per_step)),
+            "achieved_gbs": round(lbs.per_step / (ms["us_per_step"] * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(lbs.per_step / (ms["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s_per_layer": round(cfg.batch / (ms["us_per_step"] * 1e-6), 1),
+            "flush_us": round(ms["flush_avg"], 2), "flush_bytes": lbs.flush_launch,
+            "flush_gbs": round(sgbs, 1),
+            "read_us": round(ms["read_avg"], 2), "read_bytes_avg": int(round(lbs.read_launch_avg)),
+            "read_gbs": round(lbs.read_launch_avg / (ms["read_avg"] * 1e-6) / 1e9, 1),
+        })
+        if baselines:
+            sm["speedup_vs_full"] = round(baselines["full_step_us"] / ms["us_per_step"], 3)
+            sm["speedup_vs_replay"] = round(baselines["replay_step_us"] / ms["us_per_step"], 3)
+        state_map = sm
+        log(f"[bench] state-dependent map: {sm}")
+    del layers
 
     # ------------------------------------------ copy-bandwidth reference
     nbytes = 2 * 2 ** 30
@@ -311,6 +353,7 @@ def main():
         },
         "baselines": baselines,
         "sketch_error": approx,
+        "state_map": state_map,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -348,17 +391,18 @@ def flush_traffic(name):
     return e["bytes"]
 
 
-def sketch_error(cfg, li, src, pool, steps):
+def sketch_error(cfg, li, src, pool, steps, coef="fixed"):
     """Relative L2 error of the sketched read against the exact read on the
     same state and inputs: one fresh layer runs the sketch path (prime, read,
-    flush when due), another the ReplaySSM step, whose outputs are exact.
+    flush when due) with the fixed or the state-dependent coefficient map,
+    another the ReplaySSM step, whose outputs are exact.
     Synthetic states and queries have no low-rank structure, so this is far
     from the pages' figures on model states; it is reported, not gated."""
     import numpy as np
     import torch
     from ssm_decode_amd import abi, feed
     from ssm_decode_amd.layer import DeviceStep
-    ls, lr = feed.make_layer(cfg, li), feed.make_layer(cfg, li)
+    ls, lr = feed.make_layer(cfg, li, coef=coef), feed.make_layer(cfg, li)
     ls.S.copy_(src.S)
     lr.S.copy_(src.S)
     assert feed.prime(ls, li) == 0

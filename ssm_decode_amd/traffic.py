@@ -13,7 +13,10 @@ Two models:
   read and written at the flush, sketch written once and read at the W-1
   other steps, ring entries appended once and re-read by later steps of the
   window, step inputs read and outputs written once, basis / coefficient
-  rows read once per launch and shared by all sequences).
+  rows read once per launch and shared by all sequences).  With the
+  state-dependent coefficient map each sequence's map (R x dk, sketch dtype)
+  is written at the flush and read at the W-1 other steps, like the sketch,
+  and only the basis remains shared.
 """
 from __future__ import annotations
 
@@ -60,10 +63,12 @@ def slot_bytes(family: str, H: int, G: int, dk: int, dv: int, act: str) -> int:
 
 
 def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R: int,
-                act: str, sketch: str) -> LayerBytes:
+                act: str, sketch: str, coef: str = "fixed") -> LayerBytes:
     a, u = ACT_BYTES[act], ACT_BYTES[sketch]
     S = H * dk * dv * 4                   # state of one sequence
     Useq = R * dv * u                     # sketch of one sequence
+    if coef == "state":                   # the sequence's own map travels with its sketch
+        Useq += R * dk * u
     slot = slot_bytes(family, H, G, dk, dv, act)
     q = G * dk * a
     o = H * dv * a
@@ -71,7 +76,8 @@ def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R
     ring_reads = W * (W - 1) // 2         # reads of earlier entries over a window
     appends = W - 1                       # entries written to the ring
     per_seq = 2 * S + W * Useq + (ring_reads + appends) * slot + W * (q + slot + o)
-    per_window = B * per_seq + W * basis
+    # shared rows: Pt at the flush, plus the fixed C at every read launch
+    per_window = B * per_seq + (W if coef == "fixed" else 1) * basis
     # flush launch: S read + write, U write, W entries read, q read, o write, Pt
     flush = B * (2 * S + Useq + W * slot + q + o) + basis
     # the W-1 non-flush reads plus the read at the flush step (append only)
@@ -84,6 +90,6 @@ def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R
                       replay_per_step=replay_window / W)
 
 
-def config_bytes(cfg, R: int) -> LayerBytes:
+def config_bytes(cfg, R: int, coef: str = "fixed") -> LayerBytes:
     return layer_bytes(cfg.family, cfg.batch, cfg.heads, cfg.qk_groups, cfg.dk, cfg.dv,
-                       cfg.window, R, cfg.act, cfg.sketch)
+                       cfg.window, R, cfg.act, cfg.sketch, coef)

@@ -74,3 +74,16 @@ def test_bytes_scale_linearly_with_batch():
 def test_sketch_beats_replay_beats_standard_per_step():
     lb = _lb()
     assert lb.per_step < lb.replay_per_step < lb.full_step
+
+
+def test_state_map_bytes():
+    """The state-dependent map adds each sequence's R x dk map (sketch dtype)
+    written at the flush and read at the other W-1 steps, and drops the
+    fixed map's shared rows from the W-1 read launches."""
+    B, H, G, dk, dv, W, R = 320, 128, 8, 128, 64, 16, 1024
+    fx = traffic.layer_bytes("mamba2", B, H, G, dk, dv, W, R, "bf16", "bf16")
+    st = traffic.layer_bytes("mamba2", B, H, G, dk, dv, W, R, "bf16", "bf16", coef="state")
+    Cseq = R * dk * 2
+    assert st.per_window - fx.per_window == B * W * Cseq - (W - 1) * R * dk * 4
+    assert st.flush_launch - fx.flush_launch == B * Cseq
+    assert st.full_step == fx.full_step and st.replay_per_step == fx.replay_per_step
