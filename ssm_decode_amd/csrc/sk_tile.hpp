@@ -80,17 +80,18 @@ struct TileLds {
   static constexpr bool CHUNK = FAM != FAM_M2 && MODE == MODE_FLUSH;
   static constexpr int DN_END = CHUNK ? GF + DK : 0;
   static constexpr int T0 = KEYS0 + (KEYS > BASIS ? KEYS : BASIS);
-  // state-dependent map (flush): each wave stages 16 state rows of its
-  // column block below the basis while the sketch is formed; once every wave
-  // is past the sketch, the partial Y blocks and Gram matrix of every wave
-  // ([wave][MB + 1][lane] of 4 floats) and the 16 x 16 inverse reuse the
-  // whole area
+  // state-dependent map (flush), used once every wave is past the sketch:
+  // each wave stages 16 state rows of its column block at a time (SST), and
+  // publishes its partial Y block of every band another wave owns (PART,
+  // [band][NCB - 1][lane] of 4 floats) and its partial Gram matrix (GP,
+  // [wave][lane]); wave 0 writes the 16 x 16 inverse (GINV)
   static constexpr int SSTR = T::CB + 4;                       // staged row stride
   static constexpr int SST = 0;
-  static constexpr int PART = 0;
-  static constexpr int GINV = PART + T::NCB * (T::MB + 1) * 256;
+  static constexpr int PART = SST + T::NCB * 16 * SSTR;
+  static constexpr int GP = PART + T::MB * (T::NCB - 1) * 256;
+  static constexpr int GINV = GP + T::NCB * 256;
   static constexpr int MAP_END = COEF ? GINV + 256 : 0;
-  static_assert(!COEF || T::NCB * 16 * SSTR <= KEYS0, "staged state rows overlap the basis");
+  static_assert(PART % 4 == 0, "LDS regions must be 16-byte aligned");
   static constexpr int T1 = T0 > DN_END ? T0 : DN_END;
   static constexpr int TOTAL = T1 > MAP_END ? T1 : MAP_END;
   static constexpr int BYTES = TOTAL * 4;
@@ -141,8 +142,9 @@ __device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
 //     v_mfma_f32_16x16x4_f32 for K-step t; for G they are the B operand too;
 //   - for Y each wave stages its 16 x 32 block of every 16-row band of S in
 //     LDS and reads it back transposed as the B operand (8 K-steps a band);
-//   - the waves' partial G and Y blocks are summed through LDS; wave 0
-//     inverts G + lambda I (Gauss-Jordan, no pivoting: the matrix is
+//   - band mb belongs to wave mb % waves, which keeps its own partial Y block
+//     in registers; the other waves publish theirs, and their partial G,
+//     through LDS; wave 0 inverts G + lambda I (Gauss-Jordan, no pivoting: the matrix is
 //     symmetric positive definite) with lane (j, i / 4) holding column j;
 //   - C = (G + lambda I)^{-1} Y is one more 4-step MFMA per 16-column band,
 //     each wave taking the bands b % waves == its index.
@@ -171,9 +173,14 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
 #pragma unroll
   for (int t = 0; t < 8; ++t) gp = mfma16x4(uh[t], uh[t], gp);
 
-  // Y blocks: band mb gives Y[4 rg + v][16 mb + cg] in lane (cg, rg)
+  // Y blocks: band mb gives Y[4 rg + v][16 mb + cg] in lane (cg, rg).  The
+  // band's owner (wave mb % NCB) keeps its partial in registers; the other
+  // waves publish theirs.
+  constexpr int MBW = (MB + NCB - 1) / NCB;
+  __syncthreads();          // every wave is past its sketch: the basis is free
   float* s_st = smem + LY::SST + wv * 16 * SSTR;
-  f32x4v yp[MB];
+  f32x4v* part = reinterpret_cast<f32x4v*>(smem + LY::PART);
+  f32x4v own[MBW];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -185,23 +192,26 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
     const float4 s0 = *reinterpret_cast<const float4*>(s_st + cg * SSTR + 8 * rg);
     const float4 s1 = *reinterpret_cast<const float4*>(s_st + cg * SSTR + 8 * rg + 4);
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    yp[mb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    f32x4v yp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) yp[mb] = mfma16x4(uh[t], sv[t], yp[mb]);
+    for (int t = 0; t < 8; ++t) yp = mfma16x4(uh[t], sv[t], yp);
+    const int owner = mb % NCB;
+    if (wv == owner) {
+      own[mb / NCB] = yp;
+    } else {
+      const int k = wv < owner ? wv : wv - 1;
+      part[(mb * (NCB - 1) + k) * 64 + lane] = yp;
+    }
   }
-
-  __syncthreads();          // every wave is past its sketch and its staging
-  f32x4v* part = reinterpret_cast<f32x4v*>(smem + LY::PART);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) part[(wv * (MB + 1) + mb) * 64 + lane] = yp[mb];
-  part[(wv * (MB + 1) + MB) * 64 + lane] = gp;
+  reinterpret_cast<f32x4v*>(smem + LY::GP)[wv * 64 + lane] = gp;
   __syncthreads();
 
   float* s_gi = smem + LY::GINV;
   if (wv == 0) {
-    f32x4v g = part[MB * 64 + lane];
+    const f32x4v* gpa = reinterpret_cast<const f32x4v*>(smem + LY::GP);
+    f32x4v g = gpa[lane];
 #pragma unroll
-    for (int w = 1; w < NCB; ++w) g += part[(w * (MB + 1) + MB) * 64 + lane];
+    for (int w = 1; w < NCB; ++w) g += gpa[w * 64 + lane];
     // lane (cg, rg) holds G[4 rg + v][cg]
     float dg = 0.f;
 #pragma unroll
@@ -237,16 +247,15 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
 #pragma unroll
     for (int v = 0; v < 4; ++v) s_gi[(4 * rg + v) * 16 + cg] = m[v];
   }
-  // each wave's own bands: sum the partial Y blocks
-  constexpr int MBW = (MB + NCB - 1) / NCB;
+  // each wave's own bands: add the other waves' partial Y blocks
   f32x4v y[MBW];
 #pragma unroll
   for (int q = 0; q < MBW; ++q) {
     const int mb = wv + q * NCB;
-    y[q] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    y[q] = own[q];
     if (mb < MB) {
 #pragma unroll
-      for (int w = 0; w < NCB; ++w) y[q] += part[(w * (MB + 1) + mb) * 64 + lane];
+      for (int k = 0; k < NCB - 1; ++k) y[q] += part[(mb * (NCB - 1) + k) * 64 + lane];
     }
   }
   __syncthreads();
