@@ -250,6 +250,18 @@ __device__ __forceinline__ float row16_prod(float x) {
   return x;
 }
 
+// Sum over each aligned group of N lanes (N = 1, 2, 4 or 8; lanes that
+// differ in their low log2 N bits); every lane of the group receives it.
+// The 8-lane step mirrors each half row, which pairs the two quads.
+template <int N>
+__device__ __forceinline__ float low_lane_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "low_lane_sum: 1, 2, 4 or 8 lanes");
+  if constexpr (N >= 2) x += dpp_f<0xB1>(x, 0.f);
+  if constexpr (N >= 4) x += dpp_f<0x4E>(x, 0.f);
+  if constexpr (N >= 8) x += dpp_f<0x141>(x, 0.f);
+  return x;
+}
+
 // Value of lane L (a compile-time or wave-uniform index) in every lane.
 __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));

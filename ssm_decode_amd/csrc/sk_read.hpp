@@ -22,38 +22,53 @@ namespace sk {
 //   n0[b][g]         = the group's ring fill, or a negative error code when
 //                      the heads of the group disagree or the fill is out of
 //                      range
-// C is shared by all sequences, so one workgroup takes CQ_NB sequences of one
-// group and reads each row of C once.
+// A fixed C is shared by all sequences, so one workgroup takes 4 sequences of
+// one group and reads each of its rows of C once.
 //
 // m2_read_kernel then needs no keys, no queries and no exchange between
 // heads: one wave per (sequence, group, block of four heads), with
 //   q~ = D q, D = prod_i a_i;   o_buf = sum_i w_i d_i v_i, w_i = dt_i prod_{t>i} a_t
 //   o  = D * U_h cq_h + o_buf
 constexpr int M2R_MAXHPG = 16;     // heads per B/C group (at most)
-constexpr int CQ_NB = 8;           // sequences per prep workgroup
+constexpr int CQ_NB = 8;           // sequences per dot-product workgroup
 constexpr int CQ_THREADS = 256;
-// Coefficient rows of a prep workgroup: the fixed map keeps a row's C
-// segment in registers across the CQ_NB sequences (4 lanes a row); the
-// state-dependent map has a row per sequence, read once (8 lanes a row keep
-// the CQ_NB rows' segments in registers at dk >= 64).
-template <int COEF, int DK>
+// The prep grid is (dot-product blocks, then coefficient blocks) x groups.
+// A coefficient block takes ROWS coefficient rows of a group for NBC
+// sequences.  The fixed map keeps a row's C chunks in registers across the
+// NBC sequences (4 lanes a row); the state-dependent map has a row per
+// sequence, read once (8 lanes a row at dk >= 64).  Larger blocks cut the L2
+// traffic of a fixed C but lengthen each workgroup's serial loop over its
+// sequences, which costs more.
+template <int COEF, int DK, typename UT>
 struct PrepGrid {
-  static constexpr int LPR = COEF && DK >= 64 ? 8 : 4;     // lanes per coefficient row
-  static constexpr int ROWS = CQ_THREADS / LPR;            // rows per workgroup
+  static constexpr int CSIZE = COEF ? (int)sizeof(UT) : 4;  // bytes per C element
+  static constexpr int NCH = DK * CSIZE / 16;               // 16-byte chunks per C row
+  static constexpr int LPR0 = COEF && DK >= 64 ? 8 : 4;
+  static constexpr int LPR = NCH < LPR0 ? NCH : LPR0;        // lanes per coefficient row
+  static constexpr int ROWS = CQ_THREADS / LPR;              // rows per workgroup
   static constexpr int ZBLOCKS = (M2R_MAXHPG * 16 + ROWS - 1) / ROWS;
+  static constexpr int NBC = 4;                              // sequences per coefficient block
+  static __host__ __device__ int dot_blocks(int B) { return (B + CQ_NB - 1) / CQ_NB; }
+  static __host__ __device__ int coef_seq_blocks(int B) { return (B + NBC - 1) / NBC; }
+  static __host__ __device__ int blocks(int B) { return dot_blocks(B) + coef_seq_blocks(B) * ZBLOCKS; }
 };
 constexpr int DOT_LPP = 4;         // lanes per (sequence, slot) dot product
 
 template <int DK, typename AT, int WMAX>
-__device__ __forceinline__ void m2_prep_dots(const Params& p) {
-  constexpr int SEGD = DK / DOT_LPP;               // key elements per lane
+__device__ __forceinline__ void m2_prep_dots(const Params& p, int xb) {
+  // a key or query row is split into NCK chunks of CEK elements (16 bytes, or
+  // a quarter row when that is smaller); lane qt of a pair takes chunks
+  // qt, qt + 4, .. so that one load instruction reads whole 64-byte pieces
+  constexpr int CEK = (16 / (int)sizeof(AT)) < DK / DOT_LPP ? 16 / (int)sizeof(AT) : DK / DOT_LPP;
+  constexpr int NCK = DK / CEK;
+  constexpr int NKL = NCK / DOT_LPP;               // chunks per lane
   constexpr int PPP = CQ_THREADS / DOT_LPP;        // pairs per pass
   constexpr int PASSES = (CQ_NB * WMAX + PPP - 1) / PPP;
-  static_assert(SEGD % 8 == 0 || SEGD == 4, "key segments are 8-element (or 4) chunks");
+  static_assert(NKL >= 1 && NCK % DOT_LPP == 0 && CEK % 2 == 0, "key rows split into lane chunks");
   const int tid = threadIdx.x;
   const int qt = tid & (DOT_LPP - 1);
   const int g = blockIdx.y;
-  const int b0 = blockIdx.x * CQ_NB;
+  const int b0 = xb * CQ_NB;
   const int nb = min(CQ_NB, p.B - b0);
   const int W = p.W, HPG = p.HPG;
   const M2Work wl(p.B, p.R, p.G, W);
@@ -82,7 +97,7 @@ __device__ __forceinline__ void m2_prep_dots(const Params& p) {
   const AT* rk = reinterpret_cast<const AT*>(p.rk);
   const AT* q = reinterpret_cast<const AT*>(p.q);
   // issue every key and query segment load, then the dot products
-  VecN<AT, SEGD> kv[PASSES], qv[PASSES];
+  VecN<AT, CEK> kv[PASSES][NKL], qv[PASSES][NKL];
   int pb[PASSES], pi[PASSES], pn0[PASSES];
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
@@ -92,17 +107,22 @@ __device__ __forceinline__ void m2_prep_dots(const Params& p) {
     pb[ps] = bb; pi[ps] = i; pn0[ps] = n0;
     const size_t bgi = (size_t)(b0 + (bb < nb ? bb : 0)) * p.G + g;
     const AT* kp = (i < n0) ? rk + (bgi * W + i) * DK : kin + bgi * DK;
-    kv[ps] = ldraw<SEGD>(kp + qt * SEGD);
-    qv[ps] = ldraw<SEGD>(q + bgi * DK + qt * SEGD);
+#pragma unroll
+    for (int k = 0; k < NKL; ++k) {
+      kv[ps][k] = ldraw<CEK>(kp + CEK * (qt + DOT_LPP * k));
+      qv[ps][k] = ldraw<CEK>(q + bgi * DK + CEK * (qt + DOT_LPP * k));
+    }
   }
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < SEGD; e += 2) {
-      a0 += vget(kv[ps], e) * vget(qv[ps], e);
-      a1 += vget(kv[ps], e + 1) * vget(qv[ps], e + 1);
-    }
+    for (int k = 0; k < NKL; ++k)
+#pragma unroll
+      for (int e = 0; e < CEK; e += 2) {
+        a0 += vget(kv[ps][k], e) * vget(qv[ps][k], e);
+        a1 += vget(kv[ps][k], e + 1) * vget(qv[ps][k], e + 1);
+      }
     float d = a0 + a1;
     d += dpp_f<0xB1>(d, 0.f);                      // quad sum: the pair's four lanes
     d += dpp_f<0x4E>(d, 0.f);
@@ -114,40 +134,52 @@ __device__ __forceinline__ void m2_prep_dots(const Params& p) {
 
 template <int DK, typename AT, typename UT, int WMAX, int COEF>
 __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
-  using PG = PrepGrid<COEF, DK>;
-  constexpr int CQ_LPR = PG::LPR, CQ_ROWS = PG::ROWS;
-  if (blockIdx.z == PG::ZBLOCKS) {                 // uniform: the dot-product block
-    m2_prep_dots<DK, AT, WMAX>(p);
+  using PG = PrepGrid<COEF, DK, UT>;
+  constexpr int CQ_LPR = PG::LPR, CQ_ROWS = PG::ROWS, NBC = PG::NBC;
+  const int ndot = PG::dot_blocks(p.B);
+  if ((int)blockIdx.x < ndot) {                    // uniform: a dot-product block
+    m2_prep_dots<DK, AT, WMAX>(p, blockIdx.x);
     return;
   }
-  constexpr int SEGC = DK / CQ_LPR;              // row elements per lane
-  constexpr int QCH = CQ_NB * DK / 4;            // 4-element query chunks per block
+  const int cb = blockIdx.x - ndot;
+  const int nxs = PG::coef_seq_blocks(p.B);
+  const int xs = cb % nxs, zb = cb / nxs;
+  // a C row is NCH chunks of 16 bytes; lane qt of the row takes chunks qt,
+  // qt + LPR, .. so that one load instruction reads whole 64- or 128-byte
+  // pieces of the rows
+  using CT = typename std::conditional<COEF != 0, UT, float>::type;
+  constexpr int CE = 16 / (int)sizeof(CT);       // elements per chunk
+  constexpr int NCL = PG::NCH / CQ_LPR;          // chunks per lane
+  static_assert(NCL >= 1 && PG::NCH % CQ_LPR == 0, "C rows split into lane chunks");
+  constexpr int QCH = NBC * DK / 4;              // 4-element query chunks per block
   constexpr int QIT = (QCH + CQ_THREADS - 1) / CQ_THREADS;
-  static_assert(SEGC % 4 == 0, "row segments are read as float4");
-  __shared__ float s_q[CQ_NB][DK];
+  __shared__ float s_q[NBC][DK];
   const int tid = threadIdx.x;
   const int g = blockIdx.y;
   const int roff0 = p.off[g * p.HPG];
   const int rows = p.off[(g + 1) * p.HPG] - roff0;
-  const int rb = blockIdx.z * CQ_ROWS;
+  const int rb = zb * CQ_ROWS;
   if (rb >= rows) return;                        // uniform: no rows in this block
-  const int b0 = blockIdx.x * CQ_NB;
-  const int nb = min(CQ_NB, p.B - b0);
+  const int b0 = xs * NBC;
+  const int nb = min(NBC, p.B - b0);
   const int row = rb + tid / CQ_LPR;
   const int qt = tid & (CQ_LPR - 1);
   // C rows: the fixed map's row once for every sequence, or the row of each
   // sequence's own map
-  constexpr int NCR = COEF ? CQ_NB : 1;
-  VecN<typename std::conditional<COEF != 0, UT, float>::type, SEGC> c[NCR];
+  constexpr int NCR = COEF ? NBC : 1;
+  VecN<CT, CE> c[NCR][NCL];
 #pragma unroll
   for (int bb = 0; bb < NCR; ++bb) {
     const int rr = row < rows ? row : 0;          // clamped: loads stay unconditional
+    const CT* rp;
     if constexpr (COEF) {
       const int b = b0 + (bb < nb ? bb : 0);
-      c[bb] = ldraw<SEGC>(reinterpret_cast<const UT*>(p.Cs) + ((size_t)b * p.R + roff0 + rr) * DK + qt * SEGC);
+      rp = reinterpret_cast<const UT*>(p.Cs) + ((size_t)b * p.R + roff0 + rr) * DK;
     } else {
-      c[bb] = ldraw<SEGC>(p.C + (size_t)(roff0 + rr) * DK + qt * SEGC);
+      rp = p.C + (size_t)(roff0 + rr) * DK;
     }
+#pragma unroll
+    for (int k = 0; k < NCL; ++k) c[bb][k] = ldraw<CE>(rp + CE * (qt + CQ_LPR * k));
   }
   const AT* q = reinterpret_cast<const AT*>(p.q);
   float qv[QIT][4];
@@ -166,20 +198,23 @@ __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
   __syncthreads();
   float* cq = reinterpret_cast<float*>(p.work);
 #pragma unroll
-  for (int bb = 0; bb < CQ_NB; ++bb) {
+  for (int bb = 0; bb < NBC; ++bb) {
     if (bb < nb) {
-      const auto& cr = c[COEF ? bb : 0];
-      const float* qs = &s_q[bb][qt * SEGC];
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-      for (int e = 0; e < SEGC; e += 4) {
-        const float4 qq = *reinterpret_cast<const float4*>(qs + e);
-        a0 += vget(cr, e) * qq.x;
-        a1 += vget(cr, e + 1) * qq.y;
-        a2 += vget(cr, e + 2) * qq.z;
-        a3 += vget(cr, e + 3) * qq.w;
+      for (int k = 0; k < NCL; ++k) {
+        const auto& cr = c[COEF ? bb : 0][k];
+        const float* qs = &s_q[bb][CE * (qt + CQ_LPR * k)];
+#pragma unroll
+        for (int e = 0; e < CE; e += 4) {
+          const float4 qq = *reinterpret_cast<const float4*>(qs + e);
+          a0 += vget(cr, e) * qq.x;
+          a1 += vget(cr, e + 1) * qq.y;
+          a2 += vget(cr, e + 2) * qq.z;
+          a3 += vget(cr, e + 3) * qq.w;
+        }
       }
-      const float acc = xsum<0, ilog2c(CQ_LPR)>((a0 + a1) + (a2 + a3));
+      const float acc = low_lane_sum<CQ_LPR>((a0 + a1) + (a2 + a3));
       if (qt == 0 && row < rows) cq[(size_t)(b0 + bb) * p.R + roff0 + row] = acc;
     }
   }
