@@ -393,28 +393,41 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
 }
 
 // ------------------------------------------------------------ GDN / KDA
-// One wave per (sequence, head) tile.  Every load is issued once the ring
-// fill is known, before any arithmetic: the step's own entry, the buffered
-// entries (keys, values, gates, betas), the coefficient rows of C (L2
-// resident) and the sketch rows of U.  The pull-back is then a chain over
-// the buffered entries held in registers, newest first:
+// One wave per (sequence, head) tile, DN_TPW tiles of one head (consecutive
+// sequences) per workgroup.  The fixed map's rows of C_h are loaded once per
+// workgroup into LDS (instead of once per wave from L2); a state-dependent
+// map is each tile's own and goes to registers.  Every load is issued once
+// the ring fill is known, before any arithmetic: the step's own entry, the
+// buffered entries (keys, values, gates, betas), the tile's own map rows and
+// the sketch rows of U.  The pull-back is then a chain over the buffered
+// entries held in registers, newest first:
 //   d = k_i . r;  o_buf += beta_i d v_i;  r <- alpha_i (r - beta_i d k_i)   (GDN)
 //                                        r <- g_i (.) (r - beta_i d k_i)    (KDA)
 // then c = C_h r and o = U_h c + o_buf.  Lane l holds the key elements
 // EK l .. EK l + EK - 1 of r and k_i and the output columns EV l .. ; the
 // per-slot scalars of slot i sit in lane i and are read with readlane.  The
 // append stores the step's entry from the registers that hold it.
+constexpr int DN_TPW = 4;            // tiles (waves) per workgroup
+
+__host__ __device__ inline int dn_read_blocks(int B, int H) { return (B + DN_TPW - 1) / DN_TPW * H; }
+
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF>
-__global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
+__global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   constexpr int EK = DK >= 64 ? DK / 64 : 1;
   constexpr int EV = DV >= 64 ? DV / 64 : 1;
   constexpr int KG = FAM == FAM_KDA ? EK : 1;    // gate elements per lane and slot
-  const int lane = threadIdx.x;
+  constexpr int NT = 64 * DN_TPW;
+  constexpr int CCH = 16 * DK / 4;               // 16-byte chunks of 16 rows of C
+  constexpr int CPT = (CCH + NT - 1) / NT;
+  __shared__ __align__(16) float s_c[COEF ? 1 : 16 * DK];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int W = p.W;
-  const int tile = blockIdx.x;
-  const int b = tile / p.H;
-  const int h = tile - b * p.H;
-  const size_t bh = (size_t)b * p.H + h;      // G == H for these families
+  const int h = blockIdx.x % p.H;
+  const int b = blockIdx.x / p.H * DN_TPW + wv;
+  const bool active = b < p.B;                   // the last block may hold fewer tiles
+  const int bcl = active ? b : p.B - 1;          // clamped, for addresses
+  const size_t bh = (size_t)bcl * p.H + h;      // G == H for these families
   const bool kl = lane * EK < DK;             // lane holds key elements
   const bool vl = lane * EV < DV;             // lane holds output columns
   // lanes without elements (small heads) load a valid element and drop it,
@@ -424,14 +437,30 @@ __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
 
   // the ring fill and the rank offsets first: every address below depends
   // on them, and the memory counter retires loads in order
-  const int n0 = p.count[bh];
+  const int n0raw = p.count[bh];
   const int off = p.off[h], rk = p.off[h + 1] - off;
-  if (n0 < 0 || n0 >= W) {
-    if (lane == 0) atomicOr(p.err, ERRBIT_COUNT);
-    return;
+  // the fixed map's rows of this head, staged through LDS once per workgroup
+  // (two named registers, not an array: a private array would be placed in
+  // LDS by the compiler, which then waits for the loads before issuing the
+  // others)
+  static_assert(CPT <= 2, "at most two 16-byte chunks of C per thread");
+  auto c_chunk = [&](int u) -> float4 {
+    const int idx = threadIdx.x + NT * u;
+    const int row = idx / (DK / 4), ch = idx - row * (DK / 4);
+    const int rr = row < rk ? row : 0;           // clamped: the load stays unconditional
+    return *reinterpret_cast<const float4*>(p.C + (size_t)(off + rr) * DK + 4 * ch);
+  };
+  float4 cst0 = make_float4(0.f, 0.f, 0.f, 0.f), cst1 = cst0;
+  if constexpr (!COEF) {
+    cst0 = c_chunk(0);
+    if constexpr (CPT > 1) cst1 = c_chunk(1);
   }
-  const int n = n0 + 1;
+  // (the loads above are issued before anything waits for the ring fill)
   __builtin_amdgcn_sched_barrier(0);
+  const bool ok = n0raw >= 0 && n0raw < W;
+  const int n0 = ok ? n0raw : 0;
+  const int n = n0 + 1;
+  const bool rd = active && ok && n < W;         // this tile writes an output
   const AT* kin = reinterpret_cast<const AT*>(p.k) + bh * DK + lk;
   const AT* vin = reinterpret_cast<const AT*>(p.v) + bh * DV + lv;
   const float* gin = reinterpret_cast<const float*>(p.gate) + (FAM == FAM_KDA ? bh * DK + lk : bh);
@@ -448,42 +477,59 @@ __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
   else gcur[0] = gin[0];
   const float bcur = p.beta[bh];
 
-  if (n < W) {
-    // ------------------------------------------------ issue the loads
-    float r[EK];
-    ldn<EK>(reinterpret_cast<const AT*>(p.q) + bh * DK + lk, r);
-    if (!kl)
+  // ------------------------------------------------ issue the loads
+  const int nr = rd ? n0 : 0;                    // buffered entries this tile reads
+  float r[EK];
+  ldn<EK>(reinterpret_cast<const AT*>(p.q) + bh * DK + lk, r);
+  if (!kl)
 #pragma unroll
-      for (int e = 0; e < EK; ++e) r[e] = 0.f;
-    VecN<AT, EK> ks[WMAX - 1];
-    VecN<AT, EV> vs[WMAX - 1];
-    float gs[WMAX - 1][KG];
+    for (int e = 0; e < EK; ++e) r[e] = 0.f;
+  VecN<AT, EK> ks[WMAX - 1];
+  VecN<AT, EV> vs[WMAX - 1];
+  float gs[WMAX - 1][KG];
 #pragma unroll
-    for (int i = 0; i < WMAX - 1; ++i) {
-      if (i < n0) {                                // uniform
-        ks[i] = ldraw<EK>(ring_k + (size_t)i * DK);
-        vs[i] = ldraw<EV>(ring_v + (size_t)i * DV);
-        if (FAM == FAM_KDA) ldn<KG>(ring_g + (size_t)i * DK, gs[i]);
-      }
+  for (int i = 0; i < WMAX - 1; ++i) {
+    if (i < nr) {                                // uniform
+      ks[i] = ldraw<EK>(ring_k + (size_t)i * DK);
+      vs[i] = ldraw<EV>(ring_v + (size_t)i * DV);
+      if (FAM == FAM_KDA) ldn<KG>(ring_g + (size_t)i * DK, gs[i]);
     }
-    // GDN / KDA per-slot scalars: slot i in lane i
-    const int ls = lane < n0 ? lane : 0;
-    const float al_l = FAM == FAM_GDN ? ring_g[ls] : 1.f;
-    const float be_l = ring_b[ls];
-    float cr[16][EK];
-    const UT* Csb = reinterpret_cast<const UT*>(p.Cs) + ((size_t)b * p.R + off) * DK + lk;
+  }
+  // GDN / KDA per-slot scalars: slot i in lane i
+  const int ls = lane < nr ? lane : 0;
+  const float al_l = FAM == FAM_GDN ? ring_g[ls] : 1.f;
+  const float be_l = ring_b[ls];
+  float cr[COEF ? 16 : 1][EK];
+  if constexpr (COEF) {
+    const UT* Csb = reinterpret_cast<const UT*>(p.Cs) + ((size_t)bcl * p.R + off) * DK + lk;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < rk) {
-        if constexpr (COEF) ldn<EK>(Csb + (size_t)j * DK, cr[j]);
-        else ldn<EK>(p.C + (size_t)(off + j) * DK + lk, cr[j]);
-      }
-    VecN<UT, EV> us[16];
-    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + lv;
+      if (j < rk && rd) ldn<EK>(Csb + (size_t)j * DK, cr[j]);
+  }
+  VecN<UT, EV> us[16];
+  const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)bcl * p.R + off) * DV + lv;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < rk) us[j] = ldraw<EV>(Ur + (size_t)j * DV);
+  for (int j = 0; j < 16; ++j)
+    if (j < rk && rd) us[j] = ldraw<EV>(Ur + (size_t)j * DV);
 
+  if constexpr (!COEF) {
+    // (every load is in flight before the wait for the staged rows)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int idx = threadIdx.x + NT * u;
+      const int row = idx / (DK / 4), ch = idx - row * (DK / 4);
+      if (idx < CCH && row < rk) *reinterpret_cast<float4*>(s_c + row * DK + 4 * ch) = u ? cst1 : cst0;
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  if (!ok) {
+    if (lane == 0) atomicOr(p.err, ERRBIT_COUNT);
+    return;
+  }
+
+  if (rd) {
     // ---------------------------------------- pull-back, newest first
     float ob[EV];
 #pragma unroll
@@ -523,12 +569,19 @@ __global__ void __launch_bounds__(64) dn_read_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < rk) {                                // uniform
+        float cj[EK];
+        if constexpr (COEF) {
+#pragma unroll
+          for (int e = 0; e < EK; ++e) cj[e] = cr[j][e];
+        } else {
+          ldn<EK>(s_c + j * DK + lk, cj);
+        }
         float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < EK; ++e) a += cr[j][e] * r[e];
-        const float cj = wave_sum(a);
+        for (int e = 0; e < EK; ++e) a += cj[e] * r[e];
+        const float c = wave_sum(a);
 #pragma unroll
-        for (int e = 0; e < EV; ++e) out[e] += cj * vget(us[j], e);
+        for (int e = 0; e < EV; ++e) out[e] += c * vget(us[j], e);
       }
     }
     if (vl) stn<EV>(reinterpret_cast<AT*>(p.o) + bh * DV + lv, out);
