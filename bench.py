@@ -210,7 +210,10 @@ def main():
         f"flush avg {flush_avg:.1f} us ({len(flush_us)} launches); read avg {read_avg:.2f} us")
 
     achieved_gbs = lb.per_step / (us_per_step * 1e-6) / 1e9
-    flush_gbs = lb.flush_launch / (flush_avg * 1e-6) / 1e9
+    # a ragged phase flushes about B / W sequences per launch (shared basis once)
+    flush_bytes = lb.flush_launch if not ragged else \
+        (lb.flush_launch - lb.basis) / W + lb.basis
+    flush_gbs = flush_bytes / (flush_avg * 1e-6) / 1e9
     read_gbs = lb.read_launch_avg / (read_avg * 1e-6) / 1e9
     windows_exact = ragged or K % W == 0
 
@@ -269,14 +272,15 @@ def main():
         layers = make_layers("state")
         ms = measure(layers)
         lbs = traffic.config_bytes(cfg, int(li.offsets[-1]), "state")
-        sgbs = lbs.flush_launch / (ms["flush_avg"] * 1e-6) / 1e9
+        sflush = lbs.flush_launch if not ragged else (lbs.flush_launch - lbs.basis) / W + lbs.basis
+        sgbs = sflush / (ms["flush_avg"] * 1e-6) / 1e9
         sm.update({
             "us_per_step": round(ms["us_per_step"], 3),
             "algorithmic_bytes_per_step": int(round(lbs.per_step)),
             "achieved_gbs": round(lbs.per_step / (ms["us_per_step"] * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(lbs.per_step / (ms["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s_per_layer": round(cfg.batch / (ms["us_per_step"] * 1e-6), 1),
-            "flush_us": round(ms["flush_avg"], 2), "flush_bytes": lbs.flush_launch,
+            "flush_us": round(ms["flush_avg"], 2), "flush_bytes": int(round(sflush)),
             "flush_gbs": round(sgbs, 1),
             "read_us": round(ms["read_avg"], 2), "read_bytes_avg": int(round(lbs.read_launch_avg)),
             "read_gbs": round(lbs.read_launch_avg / (ms["read_avg"] * 1e-6) / 1e9, 1),
@@ -337,7 +341,7 @@ def main():
         "algorithmic_bytes_per_step": int(round(lb.per_step)),
         "kernels": {
             "flush_us": round(flush_avg, 2), "flush_launches": len(flush_us),
-            "flush_bytes": lb.flush_launch, "flush_gbs": round(flush_gbs, 1),
+            "flush_bytes": int(round(flush_bytes)), "flush_gbs": round(flush_gbs, 1),
             "read_us": round(read_avg, 2), "read_launches": len(read_us),
             "read_bytes_avg": int(round(lb.read_launch_avg)), "read_gbs": round(read_gbs, 1),
             "timing": "eager launches bracketed by HIP events on the launch stream",

@@ -46,6 +46,7 @@ class LayerBytes:
     read_launch_avg: float   # average bytes of one non-flush read launch
     full_step: int           # bytes of one standard full-state step
     replay_per_step: float   # ReplaySSM bytes per step, W-amortised
+    basis: int               # shared basis rows read by a flush launch
 
 
 def slot_bytes(family: str, H: int, G: int, dk: int, dv: int, act: str) -> int:
@@ -87,7 +88,7 @@ def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R
     replay_window = B * (W * S + S + (ring_reads + appends) * slot + W * (q + slot + o))
     return LayerBytes(per_window=per_window, per_step=per_window / W, flush_launch=flush,
                       read_launch_avg=read_total / W, full_step=full,
-                      replay_per_step=replay_window / W)
+                      replay_per_step=replay_window / W, basis=basis)
 
 
 def config_bytes(cfg, R: int, coef: str = "fixed") -> LayerBytes:
