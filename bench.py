@@ -369,12 +369,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2894228141,
-                "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
-    "gdn_b256": {"bytes": 1156135646,
-                 "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
-    "kda_b256": {"bytes": 1330880768,
-                 "src_sha256": "e50f72650a22b6c586441e150f641baa176a1988fd8bd88572630f9d36291d56"},
+    "m2_b320": {"bytes": 2894152981,
+                "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
+    "gdn_b256": {"bytes": 1156118148,
+                 "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
+    "kda_b256": {"bytes": 1330910974,
+                 "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
