@@ -51,7 +51,7 @@ _IP = C.POINTER(C.c_int)
 class _Tiles(C.Structure):
     _fields_ = [("n", C.c_int), ("rank", _IP), ("S", _DP), ("U", _DP), ("Pt", _DP),
                 ("C", _DP), ("A", _DP), ("rk", _DP), ("rv", _DP), ("rg", _DP),
-                ("rb", _DP), ("count", _IP)]
+                ("rb", _DP), ("count", _IP), ("Sc", _DP)]
 
 
 class _Step(C.Structure):
@@ -105,6 +105,8 @@ class OracleLayer:
     tiles: [n, 2] array of (b, h); S0: [n][dk][dv] initial state of those
     tiles; stores: rounding at the state / sketch / output stores ("exact",
     "f32", "bf16"); qk_groups: heads per B/C group for the k/q gather.
+    A head of rank 0 is a dense-fallback head: its flush stores the state in
+    the sketch dtype (Sc) and its reads take S^T q~ from that copy.
     coef: "fixed" reads the per-head table Cmap; "state" makes every flush
     write each tile's own map from its new state (Cmap is then ignored) with
     the relative ridge ``ridge``; the map is stored in the sketch dtype.
@@ -135,6 +137,7 @@ class OracleLayer:
         self.A = None if A is None else np.ascontiguousarray(np.asarray(A, dtype=np.float64)[hh])
         self.S = np.ascontiguousarray(np.asarray(S0, dtype=np.float64).reshape(n, dk, dv)).copy()
         self.U = np.zeros((n, self.rmax, dv))
+        self.Sc = np.zeros((n, dk, dv))          # state copies of rank-0 (dense-fallback) tiles
         self.gl = dk if family == "kda" else 1
         self.rk = np.zeros((n, W, dk))
         self.rv = np.zeros((n, W, dv))
@@ -150,7 +153,7 @@ class OracleLayer:
     def _tiles_struct(self):
         return _Tiles(self.n, _p(self.rank, _IP), _p(self.S), _p(self.U), _p(self.Pt),
                       _p(self.C), _p(self.A), _p(self.rk), _p(self.rv), _p(self.rg),
-                      _p(self.rb), _p(self.count, _IP))
+                      _p(self.rb), _p(self.count, _IP), _p(self.Sc))
 
     def gather_step(self, step, seq_rows: Optional[np.ndarray] = None):
         """Per-tile arrays from a layer-shaped StepInputs (rows = sequences).

@@ -21,6 +21,9 @@
  *    project page error objective; Mamba-2 has decay only, App. C.1);
  *  - ReplaySSM: buffered writes, full-state read each step (paper Sec. 1-2,
  *    App. D);
+ *  - dense-fallback heads (rank 0) keep a copy of the state in the sketch
+ *    dtype instead of a sketch: the flush writes it, the non-flush read
+ *    takes S^T q~ from it (paper App. D: such heads read a bf16 state copy);
  *  - the coefficient map C is either a fixed per-head table (the paper's
  *    fixed-coefficient rule, App. G) or, as the project page's per-window
  *    flush panel has it, the state-dependent map C = (U^T U)^+ U^T S0^T
@@ -78,6 +81,8 @@ typedef struct {
     double* rg;          /* [n][W] (Mamba-2 dt, GDN alpha) or [n][W][dk] (KDA g) */
     double* rb;          /* [n][W] GDN/KDA beta (unused for Mamba-2) */
     int* count;          /* [n] entries buffered since the last flush */
+    double* Sc;          /* [n][dk][dv] state copy of dense-fallback tiles (rank 0), stored
+                            in the sketch dtype; may be NULL when no tile has rank 0 */
 } orc_tiles;
 
 typedef struct {
@@ -267,6 +272,12 @@ static void build_sketch(const orc_layer* L, orc_tiles* T, int i, const double* 
     free(u);
 }
 
+/* Dense-fallback tile: the updated state, stored in the sketch dtype. */
+static void store_copy(const orc_layer* L, orc_tiles* T, int i, const double* S) {
+    double* dst = T->Sc + (size_t)i * L->dk * L->dv;
+    for (int e = 0; e < L->dk * L->dv; ++e) dst[e] = store(L->sketch_store, S[e]);
+}
+
 /* State-dependent coefficient map of tile i from its updated state S (dk x dv,
  * fp64) and the sketch rows u_j just stored (r x dv, as rounded at the store).
  * The non-flush read wants the coefficients c that best reproduce S^T q~ from
@@ -380,8 +391,12 @@ int orc_flush(const orc_layer* L, orc_tiles* T, const orc_step* st, int all) {
         memcpy(S0, S, sizeof(double) * sz);
         apply_ring(L, T, i, n, S);
         store_state(L, T, i, S);
-        build_sketch(L, T, i, S);
-        if (L->coef_mode == ORC_COEF_STATE) build_coef_map(L, T, i, S, S0);
+        if (T->rank[i] == 0) {
+            store_copy(L, T, i, S);
+        } else {
+            build_sketch(L, T, i, S);
+            if (L->coef_mode == ORC_COEF_STATE) build_coef_map(L, T, i, S, S0);
+        }
         if (st && st->o) {
             state_read(L, g_mutation == 10 ? S0 : S, st->q + (size_t)i * L->dk, o);
             write_out(L, st, i, o);
@@ -395,7 +410,8 @@ int orc_flush(const orc_layer* L, orc_tiles* T, const orc_step* st, int all) {
 }
 
 /* Sketched read (non-flush step): append the step's entry; if the window is
- * not yet full, o = U (C q~) + o_buf from the stored sketch.  When the
+ * not yet full, o = U (C q~) + o_buf from the stored sketch (a dense-fallback
+ * tile: o = Sc^T q~ + o_buf from its stored state copy).  When the
  * append fills the window (count == W) no output is written here: the flush
  * produces it. */
 int orc_read(const orc_layer* L, orc_tiles* T, const orc_step* st) {
@@ -417,8 +433,11 @@ int orc_read(const orc_layer* L, orc_tiles* T, const orc_step* st) {
         const double* U = TU(T, L, i);
         for (int j = 0; j < r; ++j)   /* c = C q~ */
             c[j] = dot(C + (size_t)j * L->dk, g_mutation == 9 ? q : qt, L->dk);
+        if (r == 0)                   /* dense fallback: o = Sc^T q~ + o_buf */
+            state_read(L, T->Sc + (size_t)i * L->dk * L->dv, g_mutation == 14 ? q : qt, o);
         for (int n2 = 0; n2 < L->dv; ++n2) {  /* o = U c + o_buf */
             double t = (g_mutation == 1) ? 0.0 : obuf[n2];
+            if (r == 0) t += o[n2];
             for (int j = 0; j < r; ++j) {
                 const int jj = (g_mutation == 4) ? (j + 1) % r : j;
                 t += U[(size_t)jj * L->dv + n2] * c[j];
