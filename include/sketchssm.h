@@ -92,7 +92,9 @@ extern "C" {
 #define SKSSM_ERRBIT_GROUP 2  /* Mamba-2 heads of one B/C group disagree on count */
 
 /* Supported shapes: (dk, dv) in {(16,32), (64,64), (128,64), (128,128)};
- * 1 <= W <= 32; 1 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16;
+ * 1 <= W <= 32; 0 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16
+ * (r_h = 0: a dense-fallback head, paper App. D, which keeps a copy of its
+ * state in the sketch dtype and reads it at non-flush steps);
  * heads % qk_groups == 0 (qk_groups == heads for GDN/KDA). */
 typedef struct {
   int32_t family;            /* SKSSM_MAMBA2 | SKSSM_GDN | SKSSM_KDA */
@@ -103,7 +105,8 @@ typedef struct {
   int32_t window;            /* W: one flush every W steps */
   int32_t act_dtype;         /* dtype of q, k, v, o, Mamba-2 dt and the ring's k, v, dt */
   int32_t sketch_dtype;      /* dtype of U */
-  const int32_t* rank_offsets_host; /* [H+1] host copy: exclusive prefix sum of r_h */
+  const int32_t* rank_offsets_host; /* [H+1] host copy: exclusive prefix sum of r_h; r_h = 0
+                                marks a dense-fallback head (no sketch: a state copy) */
   int32_t coef_map;          /* SKSSM_COEF_FIXED or SKSSM_COEF_STATE */
   float coef_ridge;          /* SKSSM_COEF_STATE: ridge relative to the mean eigenvalue of
                                 the sketch's Gram matrix, lambda = coef_ridge * trace(G) / r_h;
@@ -133,6 +136,10 @@ typedef struct {
   void* Cstate;              /* SKSSM_COEF_STATE: [B][R][dk] sketch dtype; rows off_h..off_h+r_h-1
                                 of sequence b hold the map of tile (b, h), written by every
                                 flush of that tile (NULL allowed for SKSSM_COEF_FIXED) */
+  void* Scopy;               /* [B][H][dk][dv] sketch dtype: the state copies of dense-fallback
+                                heads (r_h = 0), written by their flush, read by their
+                                non-flush reads; other heads' tiles are not touched.  NULL
+                                allowed when no head has r_h = 0 */
 } sketchssm_buffers;
 
 typedef struct {             /* one decode step */
@@ -148,8 +155,9 @@ typedef struct {             /* one decode step */
 /* Non-flush sketched read (project page, per-step non-flush panel: c = C q~,
  * o^ = U c, plus the exact buffered contribution; paper Sec. 3.2 and
  * App. C.1 for q~).  For every tile: append the step's (k, v, gate, beta) at
- * ring slot count, count += 1; if count < W write o = U (C q~) + o_buf,
- * otherwise leave o for sketchssm_flush.  Never reads S.  C is bufs->C
+ * ring slot count, count += 1; if count < W write o = U (C q~) + o_buf
+ * (a dense-fallback head: o = Scopy^T q~ + o_buf), otherwise leave o for
+ * sketchssm_flush.  Never reads S.  C is bufs->C
  * (SKSSM_COEF_FIXED) or the tile's own map in bufs->Cstate, as its last
  * flush wrote it (SKSSM_COEF_STATE).  Mamba-2 layers need bufs->work
  * (sketchssm_workspace_bytes). */
@@ -161,6 +169,8 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * SKSSM_FLUSH_DUE) or every tile (SKSSM_FLUSH_ALL): apply the count buffered
  * entries to S in order, write S, write U = S^T P from the updated state,
  * set count = 0 and, if step != NULL, write the exact output o = S^T q.
+ * A dense-fallback head (r_h = 0) writes its state copy to bufs->Scopy
+ * (rounded to the sketch dtype) instead of a sketch.
  * FLUSH_ALL with count == 0 primes U from the current state.
  * SKSSM_COEF_STATE: also write the tile's map to bufs->Cstate, solved in
  * fp32 from the sketch rows as stored (rounded to the sketch dtype) and the

@@ -39,7 +39,7 @@ class sketchssm_buffers(C.Structure):
                 ("rank_offsets", C.c_void_p), ("ring_k", C.c_void_p), ("ring_v", C.c_void_p),
                 ("ring_gate", C.c_void_p), ("ring_beta", C.c_void_p), ("count", C.c_void_p),
                 ("A", C.c_void_p), ("err", C.c_void_p), ("work", C.c_void_p),
-                ("Cstate", C.c_void_p)]
+                ("Cstate", C.c_void_p), ("Scopy", C.c_void_p)]
 
 
 class sketchssm_step(C.Structure):

@@ -26,7 +26,14 @@ bool shape_supported(int dk, int dv) {
 struct Needs {
   bool S, U, Pt, C, ring, count, step_in, step_q, step_o, work;
   bool Cstate;   // writes (flush) or reads (read) the state-dependent maps
+                 // and the state copies of dense-fallback heads
 };
+
+bool any_dense(const sketchssm_layer* L) {
+  for (int h = 0; h < L->heads; ++h)
+    if (L->rank_offsets_host[h + 1] == L->rank_offsets_host[h]) return true;
+  return false;
+}
 
 // Workspace of a Mamba-2 read (layout in sk_params.hpp): the query in every
 // head's basis, the key-query dot products and the checked ring fill.
@@ -61,7 +68,7 @@ int check_layer(const sketchssm_layer* L) {
   const int rmax = L->dk < kMaxRank ? L->dk : kMaxRank;
   for (int h = 0; h < L->heads; ++h) {
     const int r = off[h + 1] - off[h];
-    if (r < 1 || r > rmax) return SKSSM_EDIM;
+    if (r < 0 || r > rmax) return SKSSM_EDIM;           // r = 0: dense fallback
   }
   return SKSSM_OK;
 }
@@ -69,12 +76,14 @@ int check_layer(const sketchssm_layer* L) {
 int check_buffers(const sketchssm_layer* L, const sketchssm_buffers* B, const sketchssm_step* S,
                   const Needs& nd) {
   if (!B) return SKSSM_EINVAL;
+  const bool rows = L->rank_offsets_host[L->heads] > 0;   // some head is sketched
   if (nd.S && !aligned16(B->S)) return SKSSM_EINVAL;
-  if (nd.U && !aligned16(B->U)) return SKSSM_EINVAL;
-  if (nd.Pt && !aligned16(B->Pt)) return SKSSM_EINVAL;
+  if (nd.U && rows && !aligned16(B->U)) return SKSSM_EINVAL;
+  if (nd.Pt && rows && !aligned16(B->Pt)) return SKSSM_EINVAL;
   const bool state_map = L->coef_map == SKSSM_COEF_STATE;
-  if (nd.C && !state_map && !aligned16(B->C)) return SKSSM_EINVAL;
-  if (nd.Cstate && state_map && !aligned16(B->Cstate)) return SKSSM_EINVAL;
+  if (nd.C && rows && !state_map && !aligned16(B->C)) return SKSSM_EINVAL;
+  if (nd.Cstate && rows && state_map && !aligned16(B->Cstate)) return SKSSM_EINVAL;
+  if (nd.Cstate && any_dense(L) && !aligned16(B->Scopy)) return SKSSM_EINVAL;
   if ((nd.U || nd.Pt || nd.C) && !aligned16(B->rank_offsets)) return SKSSM_EINVAL;
   if (nd.ring) {
     if (!aligned16(B->ring_k) || !aligned16(B->ring_v) || !aligned16(B->ring_gate)) return SKSSM_EINVAL;
@@ -117,6 +126,7 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.err = B->err;
   p.work = B->work;
   p.Cs = B->Cstate;
+  p.Sc = B->Scopy;
   p.ridge = L->coef_ridge;
   if (S) {
     p.q = S->q;

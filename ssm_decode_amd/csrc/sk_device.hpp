@@ -219,6 +219,18 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, int voff, int s
   }
 }
 
+// Two consecutive elements, rounded to T, stored through a buffer resource
+// (fp32: 8 bytes; bf16: 4 bytes, packed).
+template <typename T>
+__device__ __forceinline__ void buf_st2(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&x)[2]) {
+  if constexpr (sizeof(T) == 4) {
+    buf_st<2>(r, voff, soff, x);
+  } else {
+    const uint32_t v = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+  }
+}
+
 // ---------------------------------------------------------- DPP reductions
 // Data-parallel-primitive moves read a neighbour lane's register inside the
 // VALU instruction (no LDS permute, no address arithmetic).  Control codes

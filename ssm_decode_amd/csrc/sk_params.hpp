@@ -28,6 +28,7 @@ struct Params {
   int32_t* err;
   void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
   void* Cs;             // state-dependent coefficient maps [B][R][dk] sketch dtype
+  void* Sc;             // state copies of dense-fallback heads [B][H][dk][dv] sketch dtype
   float ridge;          // relative ridge of the state-dependent map
   const void* q;
   const void* k;

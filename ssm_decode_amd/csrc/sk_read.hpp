@@ -369,6 +369,30 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) ob[c] += ecur * vget(vcur, c);
     }
+    if (r == 0 && hv) {
+      // dense-fallback head: acc = Scopy^T q, placed last (the sketch rows
+      // and ring values are dead by then) and 4 rows in flight, so that the
+      // path costs the kernel no registers; the query's elements go round
+      // the head's lanes through LDS, 16 at a time
+      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + s * CPL;
+      const AT* qg = reinterpret_cast<const AT*>(p.q) + bg * DK;
+#pragma unroll 1
+      for (int m0 = 0; m0 < DK; m0 += 16) {
+        ch[s] = ld(qg + m0 + s);
+#pragma unroll 1
+        for (int j0 = 0; j0 < 16; j0 += 4) {       // 4 rows in flight: few registers
+          VecN<UT, CPL> sr[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sr[j] = ldraw<CPL>(Sr + (size_t)(m0 + j0 + j) * DV);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float qj = ch[j0 + j];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] += qj * vget(sr[j], c);
+          }
+        }
+      }
+    }
     float out[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
@@ -452,8 +476,10 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   };
   float4 cst0 = make_float4(0.f, 0.f, 0.f, 0.f), cst1 = cst0;
   if constexpr (!COEF) {
-    cst0 = c_chunk(0);
-    if constexpr (CPT > 1) cst1 = c_chunk(1);
+    if (rk > 0) {                                // a dense-fallback head has no rows
+      cst0 = c_chunk(0);
+      if constexpr (CPT > 1) cst1 = c_chunk(1);
+    }
   }
   // (the loads above are issued before anything waits for the ring fill)
   __builtin_amdgcn_sched_barrier(0);
@@ -582,6 +608,23 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
         const float c = wave_sum(a);
 #pragma unroll
         for (int e = 0; e < EV; ++e) out[e] += c * vget(us[j], e);
+      }
+    }
+    if (rk == 0) {
+      // dense-fallback head: out += Scopy^T r, 16 rows at a time, each r_m
+      // read from the lane that holds it
+      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + lv;
+#pragma unroll 1
+      for (int m0 = 0; m0 < DK; m0 += 16) {
+        VecN<UT, EV> sr[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sr[j] = ldraw<EV>(Sr + (size_t)(m0 + j) * DV);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float rm = lane_value(r[j % EK], (m0 + j) / EK);
+#pragma unroll
+          for (int e = 0; e < EV; ++e) out[e] += rm * vget(sr[j], e);
+        }
       }
     }
     if (vl) stn<EV>(reinterpret_cast<AT*>(p.o) + bh * DV + lv, out);

@@ -888,8 +888,24 @@ tile_kernel(Params p) {
           stn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
       }
 
+    // ------------- dense-fallback head (rank 0): the state copy instead
+    // (stored through a buffer resource: one lane offset instead of a
+    // pointer per row, which would hold registers across the kernel)
+    if (want_u && r == 0) {                        // uniform over the workgroup
+      static_assert(NCC == 2, "the state copy stores two columns per lane");
+      const __amdgpu_buffer_rsrc_t c_rsrc =
+          make_rsrc(reinterpret_cast<UT*>(p.Sc) + bh * DK * DV, DK * DV * (int)sizeof(UT));
+      const int c_lane = (4 * rg * DV + colbase) * (int)sizeof(UT);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float x[2] = {sacc[mb][0][v], sacc[mb][1][v]};
+          buf_st2<UT>(c_rsrc, c_lane, (16 * mb + v) * DV * (int)sizeof(UT), x);
+        }
+    }
     // --------------------------- sketch U = S^T P on the matrix cores
-    if (want_u) {
+    if (want_u && r > 0) {
       float4 pr[PU];
 #pragma unroll
       for (int u = 0; u < PU; ++u) {

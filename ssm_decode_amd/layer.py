@@ -68,6 +68,9 @@ class DecodeLayer:
         self.Pt = z((self.R, dk), torch.float32)
         self.Cmap = z((self.R, dk), torch.float32)
         self.Cstate = z((B, self.R, dk), ut) if coef == "state" else None
+        # state copies of dense-fallback heads (rank 0), when there are any
+        dense = bool((np.diff(self.offsets_host) == 0).any())
+        self.Scopy = z((B, H, dk, dv), ut) if dense else None
         self.offsets = torch.from_numpy(self.offsets_host.copy()).to(device)
         self.ring_k = z((B, G, W, dk), at)
         self.ring_v = z((B, H, W, dv), at)
@@ -96,7 +99,8 @@ class DecodeLayer:
         self._bufs = abi.sketchssm_buffers(
             _ptr(self.S), _ptr(self.U), _ptr(self.Pt), _ptr(self.Cmap), _ptr(self.offsets),
             _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_gate), _ptr(self.ring_beta),
-            _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work), _ptr(self.Cstate))
+            _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work), _ptr(self.Cstate),
+            _ptr(self.Scopy))
 
     # -------------------------------------------------------------- structs
     @property

@@ -31,6 +31,7 @@ class LayerConfig:
     seed: int
     rank_lo: int = 2
     rank_hi: int = 16
+    dense_heads: tuple = ()   # heads set to rank 0 (dense fallback) after the draw
 
     @property
     def total_rank(self) -> int:

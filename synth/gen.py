@@ -171,6 +171,8 @@ def make_basis(cfg: LayerConfig, ranks: np.ndarray) -> np.ndarray:
     Pt = np.zeros((int(off[-1]), cfg.dk), dtype=np.float64)
     for h, r in enumerate(ranks):
         r = int(r)
+        if r == 0:
+            continue
         cnt = (np.arange(cfg.dk * r, dtype=np.uint64)
                + np.uint64(h * cfg.dk * cfg.dk))
         G = normal(cfg.seed, STREAM["basis"], cnt).reshape(cfg.dk, r)
@@ -210,6 +212,9 @@ class LayerInputs:
 
 def make_layer_inputs(cfg: LayerConfig) -> LayerInputs:
     ranks = draw_ranks(cfg)
+    if cfg.dense_heads:                       # dense-fallback heads: rank 0
+        ranks = ranks.copy()
+        ranks[list(cfg.dense_heads)] = 0
     off = rank_offsets(ranks)
     Pt = make_basis(cfg, ranks)
     A = None

@@ -42,6 +42,7 @@ class ParityReport:
     max_S: float = 0.0
     max_U: float = 0.0
     max_C: float = 0.0
+    max_Sc: float = 0.0
     flushes: int = 0
     count_mismatch: int = 0
     err_word: int = 0
@@ -51,6 +52,7 @@ class ParityReport:
     def line(self) -> str:
         return (f"{self.name} {self.method}: steps={self.steps} tiles={self.tiles} "
                 f"max rel-L2 o={self.max_o:.3e} S={self.max_S:.3e} U={self.max_U:.3e} C={self.max_C:.3e} "
+                f"Scopy={self.max_Sc:.3e} "
                 f"flush-steps={self.flushes} count-mismatch={self.count_mismatch} "
                 f"err={self.err_word} ({self.seconds:.1f}s)")
 
@@ -112,7 +114,8 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
             off, r = li.offsets[h], li.ranks[h]
             Cg.append(C_gpu[i, off:off + r])
             Co.append(orc.C[ti, :r])
-        rep.max_C = max(rep.max_C, rel_l2(np.concatenate(Cg), np.concatenate(Co)))
+        if Cg and sum(c.size for c in Cg):
+            rep.max_C = max(rep.max_C, rel_l2(np.concatenate(Cg), np.concatenate(Co)))
 
     if method == "sketch" and coef == "state":
         torch.cuda.synchronize()
@@ -171,9 +174,16 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
                     off, r = li.offsets[h], li.ranks[h]
                     Ug.append(U_gpu[i, off:off + r])
                     Uo.append(orc.U[ti, :r])
-                rep.max_U = max(rep.max_U, rel_l2(np.concatenate(Ug), np.concatenate(Uo)))
+                if Ug and sum(u.size for u in Ug):
+                    rep.max_U = max(rep.max_U, rel_l2(np.concatenate(Ug), np.concatenate(Uo)))
                 if coef == "state":
                     compare_maps(sel)
+                dense = [ti for ti in sel if li.ranks[tiles[ti, 1]] == 0]
+                if dense:                           # dense-fallback tiles: their state copies
+                    db = torch.from_numpy(tiles[dense, 0]).to(lay.device)
+                    dh = torch.from_numpy(tiles[dense, 1]).to(lay.device)
+                    Sc_gpu = lay.Scopy[db, dh].float().cpu().numpy().astype(np.float64)
+                    rep.max_Sc = max(rep.max_Sc, rel_l2(Sc_gpu, orc.Sc[dense]))
         if log and (t % 16 == 15 or t == steps - 1):
             print(f"  [{cfg.name} {rep.method}] step {t + 1}/{steps} max o={rep.max_o:.2e} "
                   f"S={rep.max_S:.2e} U={rep.max_U:.2e} C={rep.max_C:.2e}", flush=True)
@@ -184,6 +194,7 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     assert rep.max_S <= TOL_F32, rep.line()
     assert rep.max_U <= t_s, rep.line()
     assert rep.max_C <= t_s, rep.line()
+    assert rep.max_Sc <= t_s, rep.line()
     assert rep.err_word == 0, rep.line()
     if log:
         print("  " + rep.line(), flush=True)

@@ -56,7 +56,8 @@ def _layer(offsets, family=abi.SKSSM_MAMBA2, batch=2, heads=4, groups=4, dk=16, 
 
 def _bufs(**over):
     f = dict(S=FAKE, U=FAKE, Pt=FAKE, C=FAKE, rank_offsets=FAKE, ring_k=FAKE, ring_v=FAKE,
-             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE, Cstate=FAKE)
+             ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE, Cstate=FAKE,
+             Scopy=FAKE)
     f.update(over)
     return abi.sketchssm_buffers(**f)
 
@@ -103,8 +104,7 @@ def test_heads_per_group_limit(lib):
     del L2
 
 
-@pytest.mark.parametrize("off", [[1, 4, 8, 12, 16], [0, 0, 4, 8, 12], [0, 4, 8, 12, 29],
-                                 [0, 4, 3, 8, 12]])
+@pytest.mark.parametrize("off", [[1, 4, 8, 12, 16], [0, 4, 8, 12, 29], [0, 4, 3, 8, 12]])
 def test_bad_rank_table(lib, off):
     assert _all_calls(_layer(off), _bufs(), _step()) == [abi.SKSSM_EDIM] * 4
 
@@ -193,3 +193,21 @@ def test_coefficient_map_mode(lib):
     Lf = _layer(OK_OFF, batch=0)
     assert _all_calls(Lf, _bufs(Cstate=None), _step()) == [0] * 4
     assert abi.sketchssm_read(_layer(OK_OFF), _bufs(C=None), _step()) == abi.SKSSM_EINVAL
+
+
+def test_dense_fallback_heads(lib):
+    """r_h = 0 marks a dense-fallback head: allowed, and then the read and
+    the flush need the state copies (Scopy); a layer with no sketched head
+    needs no U, basis or map."""
+    L = _layer([0, 4, 4, 8, 12])                   # head 1 is dense
+    assert abi.sketchssm_read(L, _bufs(Scopy=None), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read(L, _bufs(Scopy=FAKE + 4), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_flush(L, _bufs(Scopy=None), None, abi.SKSSM_FLUSH_ALL) == abi.SKSSM_EINVAL
+    L0 = _layer([0, 4, 4, 8, 12], batch=0)
+    assert _all_calls(L0, _bufs(), _step()) == [0] * 4
+    assert abi.sketchssm_full_step(_layer([0, 4, 4, 8, 12]), _bufs(Scopy=None), None) == abi.SKSSM_EINVAL
+    Ld = _layer([0, 0, 0, 0, 0], batch=0)            # every head dense: R = 0
+    assert _all_calls(Ld, _bufs(U=None, Pt=None, C=None, Cstate=None), _step()) == [0] * 4
+    assert abi.sketchssm_workspace_bytes(_layer([0, 0, 0, 0, 0])) == _m2_work_bytes(2, 0, 4, 4)
+    # with sketched heads the sketch is still required
+    assert abi.sketchssm_read(_layer([0, 4, 4, 8, 12]), _bufs(U=None), _step()) == abi.SKSSM_EINVAL
