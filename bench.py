@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip full/replay GPU baselines")
     ap.add_argument("--no-state-map", action="store_true",
                     help="skip the run with the state-dependent coefficient map")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the run with dense-fallback heads")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
     ap.add_argument("--cpu-windows", type=int, default=16, help="windows in the CPU sample")
     return ap.parse_args()
@@ -85,12 +87,13 @@ def main():
     feed.fill_state(first, cfg, numpy_all=False)
     S_init = first.S.clone()
 
-    def make_layers(coef):
+    def make_layers(coef, cfg_=None, li_=None):
+        cfg_, li_ = cfg_ or cfg, li_ or li
         out = []
         for _ in range(L):
-            lay = feed.make_layer(cfg, li, device=dev, coef=coef)
+            lay = feed.make_layer(cfg_, li_, device=dev, coef=coef)
             lay.S.copy_(S_init)
-            assert feed.prime(lay, li) == 0
+            assert feed.prime(lay, li_) == 0
             out.append(lay)
         torch.cuda.synchronize()
         return out
@@ -292,6 +295,27 @@ def main():
         log(f"[bench] state-dependent map: {sm}")
     del layers
 
+    # ------ dense-fallback heads: the same workload with 1 head in 32 dense
+    # (the pages' allocation for one of their models keeps about 3% of the
+    # heads dense)
+    dense_block = None
+    if not args.no_dense:
+        torch.cuda.empty_cache()
+        dh = tuple(range(0, cfg.heads, 32))
+        cfg_d = cfg.with_(dense_heads=dh)
+        li_d = synth.make_layer_inputs(cfg_d)
+        layers = make_layers("fixed", cfg_d, li_d)
+        md = measure(layers)
+        lbd = traffic.config_bytes(cfg_d, int(li_d.offsets[-1]))
+        dense_block = {
+            "dense_heads": list(dh), "us_per_step": round(md["us_per_step"], 3),
+            "algorithmic_bytes_per_step": int(round(lbd.per_step)),
+            "achieved_gbs": round(lbd.per_step / (md["us_per_step"] * 1e-6) / 1e9, 1),
+            "flush_us": round(md["flush_avg"], 2), "read_us": round(md["read_avg"], 2),
+        }
+        log(f"[bench] dense-fallback heads: {dense_block}")
+        del layers
+
     # ------------------------------------------ copy-bandwidth reference
     nbytes = 2 * 2 ** 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -358,6 +382,7 @@ def main():
         "baselines": baselines,
         "sketch_error": approx,
         "state_map": state_map,
+        "dense_fallback": dense_block,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -16,7 +16,9 @@ Two models:
   rows read once per launch and shared by all sequences).  With the
   state-dependent coefficient map each sequence's map (R x dk, sketch dtype)
   is written at the flush and read at the W-1 other steps, like the sketch,
-  and only the basis remains shared.
+  and only the basis remains shared.  A dense-fallback head (rank 0) has no
+  sketch: its state copy (dk x dv, sketch dtype) is written at the flush and
+  read at the W-1 other steps.
 """
 from __future__ import annotations
 
@@ -64,12 +66,13 @@ def slot_bytes(family: str, H: int, G: int, dk: int, dv: int, act: str) -> int:
 
 
 def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R: int,
-                act: str, sketch: str, coef: str = "fixed") -> LayerBytes:
+                act: str, sketch: str, coef: str = "fixed", dense: int = 0) -> LayerBytes:
     a, u = ACT_BYTES[act], ACT_BYTES[sketch]
     S = H * dk * dv * 4                   # state of one sequence
     Useq = R * dv * u                     # sketch of one sequence
     if coef == "state":                   # the sequence's own map travels with its sketch
         Useq += R * dk * u
+    Useq += dense * dk * dv * u           # state copies of dense-fallback heads
     slot = slot_bytes(family, H, G, dk, dv, act)
     q = G * dk * a
     o = H * dv * a
@@ -93,4 +96,4 @@ def layer_bytes(family: str, B: int, H: int, G: int, dk: int, dv: int, W: int, R
 
 def config_bytes(cfg, R: int, coef: str = "fixed") -> LayerBytes:
     return layer_bytes(cfg.family, cfg.batch, cfg.heads, cfg.qk_groups, cfg.dk, cfg.dv,
-                       cfg.window, R, cfg.act, cfg.sketch, coef)
+                       cfg.window, R, cfg.act, cfg.sketch, coef, len(cfg.dense_heads))

@@ -87,3 +87,13 @@ def test_state_map_bytes():
     assert st.per_window - fx.per_window == B * W * Cseq - (W - 1) * R * dk * 4
     assert st.flush_launch - fx.flush_launch == B * Cseq
     assert st.full_step == fx.full_step and st.replay_per_step == fx.replay_per_step
+
+
+def test_dense_head_bytes():
+    """A dense-fallback head moves its state copy where a sketched head moves
+    its sketch: written at the flush and read at the other W-1 steps."""
+    B, H, G, dk, dv, W = 320, 128, 8, 128, 64, 16
+    base = traffic.layer_bytes("mamba2", B, H, G, dk, dv, W, 1024, "bf16", "bf16")
+    d4 = traffic.layer_bytes("mamba2", B, H, G, dk, dv, W, 1024, "bf16", "bf16", dense=4)
+    assert d4.per_window - base.per_window == B * W * 4 * dk * dv * 2
+    assert d4.flush_launch - base.flush_launch == B * 4 * dk * dv * 2
