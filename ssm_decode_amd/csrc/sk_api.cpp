@@ -127,6 +127,14 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.work = B->work;
   p.Cs = B->Cstate;
   p.Sc = B->Scopy;
+  // dense-fallback heads (r_h = 0), listed for the kernels that take only them
+  int nd = 0;
+  for (int h = 0; h < L->heads; ++h)
+    if (L->rank_offsets_host[h + 1] == L->rank_offsets_host[h]) {
+      if (nd < sk::DENSE_LIST_MAX) p.dense_list[nd] = (int16_t)h;
+      ++nd;
+    }
+  p.ndense = nd <= sk::DENSE_LIST_MAX ? nd : -1;
   p.ridge = L->coef_ridge;
   if (S) {
     p.q = S->q;

@@ -11,6 +11,8 @@ enum Mode { MODE_FLUSH = 0, MODE_FULL = 1, MODE_REPLAY = 2, MODE_READ = 3 };
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 enum ErrBit { ERRBIT_COUNT = 1, ERRBIT_GROUP = 2 };
 
+constexpr int DENSE_LIST_MAX = 64;   // dense-fallback heads listed in the kernel arguments
+
 struct Params {
   int B, H, G, HPG, W, R;
   int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
@@ -29,6 +31,9 @@ struct Params {
   void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
   void* Cs;             // state-dependent coefficient maps [B][R][dk] sketch dtype
   void* Sc;             // state copies of dense-fallback heads [B][H][dk][dv] sketch dtype
+  int ndense;           // dense-fallback heads: 0 none; > 0 their count, listed in dense_list;
+                        // -1 more than DENSE_LIST_MAX (kernels check every head)
+  int16_t dense_list[DENSE_LIST_MAX];
   float ridge;          // relative ridge of the state-dependent map
   const void* q;
   const void* k;

@@ -369,34 +369,11 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) ob[c] += ecur * vget(vcur, c);
     }
-    if (r == 0 && hv) {
-      // dense-fallback head: acc = Scopy^T q, placed last (the sketch rows
-      // and ring values are dead by then) and 4 rows in flight, so that the
-      // path costs the kernel no registers; the query's elements go round
-      // the head's lanes through LDS, 16 at a time
-      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + s * CPL;
-      const AT* qg = reinterpret_cast<const AT*>(p.q) + bg * DK;
-#pragma unroll 1
-      for (int m0 = 0; m0 < DK; m0 += 16) {
-        ch[s] = ld(qg + m0 + s);
-#pragma unroll 1
-        for (int j0 = 0; j0 < 16; j0 += 4) {       // 4 rows in flight: few registers
-          VecN<UT, CPL> sr[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sr[j] = ldraw<CPL>(Sr + (size_t)(m0 + j0 + j) * DV);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float qj = ch[j0 + j];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[c] += qj * vget(sr[j], c);
-          }
-        }
-      }
-    }
     float out[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
-    if (hv) stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
+    // (a dense-fallback head's output comes from m2_dense_read_kernel)
+    if (hv && r > 0) stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
   }
   if (n0c < 0) {                                 // the prep kernel found a bad group
     if (tid == 0 && wq == 0) atomicOr(p.err, -n0c);
@@ -413,6 +390,103 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
       reinterpret_cast<AT*>(p.rg)[bh * W + n0] = dtcur;
       p.count[bh] = n;
     }
+  }
+}
+
+// Dense-fallback heads (rank 0) of a Mamba-2 layer at a non-flush step:
+// one wave per (sequence, dense head), launched after m2_read_kernel (which
+// appends the step's entry and leaves these heads' outputs alone):
+//   o = D * Scopy^T q + sum_i w_i d_i v_i,
+// with the dot products d_i and the checked ring fill from the prep
+// kernel's workspace.  The head's state copy is read in one pass, every
+// 16-byte chunk in flight at once: lane l takes chunk l % LPRW of rows
+// l / LPRW + RPP i, and the lanes of a chunk column are summed at the end.
+template <int DK, int DV, typename AT, typename UT, int WMAX>
+__global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
+  constexpr int CE = 16 / (int)sizeof(UT);           // elements per chunk
+  constexpr int LPRW = DV / CE;                      // lanes per row
+  constexpr int RPP = 64 / LPRW;                     // rows per pass
+  constexpr int NP = DK / RPP;                       // passes
+  static_assert(LPRW >= 1 && LPRW <= 64 && DK % RPP == 0, "state copy split into lane chunks");
+  __shared__ float s_q[DK];
+  const int lane = threadIdx.x;
+  const int nd = p.ndense > 0 ? p.ndense : p.H;     // a list of dense heads, or every head
+  const int b = blockIdx.x / nd;
+  const int h = p.ndense > 0 ? p.dense_list[blockIdx.x - b * nd] : blockIdx.x - b * nd;
+  if (p.off[h + 1] != p.off[h]) return;             // (every-head grid) a sketched head
+  const int W = p.W;
+  const int g = h / p.HPG;
+  const size_t bg = (size_t)b * p.G + g, bh = (size_t)b * p.H + h;
+  const M2Work wl(p.B, p.R, p.G, W);
+  const int n0c = reinterpret_cast<const int*>(reinterpret_cast<const float*>(p.work) + wl.n0)[bg];
+  if (n0c < 0 || n0c + 1 >= W) return;               // a bad group (reported), or the flush step
+  const int n0 = n0c, n = n0 + 1;
+  const int cc = lane % LPRW, r0 = lane / LPRW;
+  __builtin_amdgcn_sched_barrier(0);
+
+  // loads: the state copy, the query, the slot gates and dot products, the
+  // ring values and the step's own value
+  const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + cc * CE;
+  VecN<UT, CE> sr[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) sr[i] = ldraw<CE>(Sr + (size_t)(r0 + RPP * i) * DV);
+  const AT* qg = reinterpret_cast<const AT*>(p.q) + bg * DK;
+  for (int m = lane; m < DK; m += 64) s_q[m] = ld(qg + m);
+  const AT* ring_dt = reinterpret_cast<const AT*>(p.rg) + bh * W;
+  const float dt = lane < n0 ? ld(ring_dt + lane) : (lane == n0 ? ld(reinterpret_cast<const AT*>(p.gate) + bh) : 0.f);
+  const float* dws = reinterpret_cast<const float*>(p.work) + wl.d + bg * W;
+  const float dl = dws[lane <= n0 ? lane : 0];
+  const AT* ring_v = reinterpret_cast<const AT*>(p.rv) + bh * W * DV + cc * CE;
+  VecN<AT, CE> vs[WMAX];
+#pragma unroll
+  for (int i = 0; i < WMAX - 1; ++i)
+    if (i < n0) vs[i] = ldraw<CE>(ring_v + (size_t)i * DV);
+  const VecN<AT, CE> vcur = ldraw<CE>(reinterpret_cast<const AT*>(p.v) + bh * DV + cc * CE);
+
+  // decays: a_i = exp(-dt_i e^A), w_i = dt_i prod_{t>i} a_t, D = prod_t a_t
+  const float a = lane < n ? m2_decay(dt, p.A[h]) : 1.0f;
+  float suf = a;                                     // inclusive suffix product
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_down(suf, d);
+    if (lane + d < 64) suf *= o;
+  }
+  const float excl = __shfl_down(suf, 1);            // prod over t > lane
+  const float e = lane < n ? dt * (lane + 1 < 64 ? excl : 1.0f) * dl : 0.f;   // w_i d_i
+  const float D = lane_value(suf, 0);
+
+  // Scopy^T q over this lane's rows, then over the lanes of its chunk column
+  __syncthreads();
+  float acc[CE];
+#pragma unroll
+  for (int c = 0; c < CE; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const float qm = s_q[r0 + RPP * i];
+#pragma unroll
+    for (int c = 0; c < CE; ++c) acc[c] += qm * vget(sr[i], c);
+  }
+#pragma unroll
+  for (int m = LPRW; m < 64; m <<= 1)
+#pragma unroll
+    for (int c = 0; c < CE; ++c) acc[c] += __shfl_xor(acc[c], m);
+
+  // the buffered term on the same columns
+  float ob[CE];
+#pragma unroll
+  for (int c = 0; c < CE; ++c) ob[c] = lane_value(e, n0) * vget(vcur, c);
+#pragma unroll
+  for (int i = 0; i < WMAX - 1; ++i)
+    if (i < n0) {
+      const float ei = lane_value(e, i);
+#pragma unroll
+      for (int c = 0; c < CE; ++c) ob[c] += ei * vget(vs[i], c);
+    }
+  if (r0 == 0) {
+    float out[CE];
+#pragma unroll
+    for (int c = 0; c < CE; ++c) out[c] = D * acc[c] + ob[c];
+    stn<CE>(reinterpret_cast<AT*>(p.o) + bh * DV + cc * CE, out);
   }
 }
 
