@@ -94,7 +94,8 @@ extern "C" {
 /* Supported shapes: (dk, dv) in {(16,32), (64,64), (128,64), (128,128)};
  * 1 <= W <= 32; 0 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16
  * (r_h = 0: a dense-fallback head, paper App. D, which keeps a copy of its
- * state in the sketch dtype and reads it at non-flush steps);
+ * state in the sketch dtype and reads it at non-flush steps; at most 64 per
+ * layer);
  * heads % qk_groups == 0 (qk_groups == heads for GDN/KDA). */
 typedef struct {
   int32_t family;            /* SKSSM_MAMBA2 | SKSSM_GDN | SKSSM_KDA */
@@ -136,10 +137,11 @@ typedef struct {
   void* Cstate;              /* SKSSM_COEF_STATE: [B][R][dk] sketch dtype; rows off_h..off_h+r_h-1
                                 of sequence b hold the map of tile (b, h), written by every
                                 flush of that tile (NULL allowed for SKSSM_COEF_FIXED) */
-  void* Scopy;               /* [B][H][dk][dv] sketch dtype: the state copies of dense-fallback
-                                heads (r_h = 0), written by their flush, read by their
-                                non-flush reads; other heads' tiles are not touched.  NULL
-                                allowed when no head has r_h = 0 */
+  void* Scopy;               /* [B][D][dk][dv] sketch dtype, D = number of dense-fallback heads
+                                (r_h = 0, at most 64), in head order: their state copies,
+                                written by their flush, read by their non-flush reads.  NULL
+                                allowed when D = 0.  (Compact: a [B][H] layout would put the
+                                few dense tiles at strides that load a few memory channels.) */
 } sketchssm_buffers;
 
 typedef struct {             /* one decode step */

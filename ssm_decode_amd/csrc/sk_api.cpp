@@ -66,10 +66,13 @@ int check_layer(const sketchssm_layer* L) {
   const int32_t* off = L->rank_offsets_host;
   if (off[0] != 0) return SKSSM_EDIM;
   const int rmax = L->dk < kMaxRank ? L->dk : kMaxRank;
+  int ndense = 0;
   for (int h = 0; h < L->heads; ++h) {
     const int r = off[h + 1] - off[h];
     if (r < 0 || r > rmax) return SKSSM_EDIM;           // r = 0: dense fallback
+    ndense += r == 0;
   }
+  if (ndense > sk::DENSE_LIST_MAX) return SKSSM_EDIM;
   return SKSSM_OK;
 }
 
@@ -128,13 +131,10 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.Cs = B->Cstate;
   p.Sc = B->Scopy;
   // dense-fallback heads (r_h = 0), listed for the kernels that take only them
-  int nd = 0;
+  int nd = 0;                          // (at most DENSE_LIST_MAX: check_layer)
   for (int h = 0; h < L->heads; ++h)
-    if (L->rank_offsets_host[h + 1] == L->rank_offsets_host[h]) {
-      if (nd < sk::DENSE_LIST_MAX) p.dense_list[nd] = (int16_t)h;
-      ++nd;
-    }
-  p.ndense = nd <= sk::DENSE_LIST_MAX ? nd : -1;
+    if (L->rank_offsets_host[h + 1] == L->rank_offsets_host[h]) p.dense_list[nd++] = (int16_t)h;
+  p.ndense = nd;
   p.ridge = L->coef_ridge;
   if (S) {
     p.q = S->q;

@@ -14,14 +14,20 @@ static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   constexpr size_t lds_flush_map = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH, 1>::BYTES;
   constexpr size_t lds_full = TileLds<FAM, DK, DV, WMAX, MODE_FULL, 0>::BYTES;
   constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY, 0>::BYTES;
-  if (mode == MODE_FLUSH && coef)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1>), grid, block, lds_flush_map, st, p);
+  // (the flush of a layer with dense-fallback heads is its own instantiation)
+  const bool dense = p.ndense > 0;
+  if (mode == MODE_FLUSH && coef && dense)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true>), grid, block, lds_flush_map, st, p);
+  else if (mode == MODE_FLUSH && coef)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false>), grid, block, lds_flush_map, st, p);
+  else if (mode == MODE_FLUSH && dense)
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true>), grid, block, lds_flush, st, p);
   else if (mode == MODE_FLUSH)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0>), grid, block, lds_flush, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false>), grid, block, lds_flush, st, p);
   else if (mode == MODE_FULL)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX, 0>), grid, block, lds_full, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FULL, WMAX, 0, false>), grid, block, lds_full, st, p);
   else if (mode == MODE_REPLAY)
-    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX, 0>), grid, block, lds_replay, st, p);
+    hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_REPLAY, WMAX, 0, false>), grid, block, lds_replay, st, p);
   else
     return -4;
   return 0;
@@ -34,9 +40,9 @@ static void launch_read(const Params& p, hipStream_t st) {
     const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
     hipLaunchKernelGGL((m2_prep_kernel<DK, AT, UT, WMAX, COEF>), pgrid, dim3(CQ_THREADS), 0, st, p);
     hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, WMAX>), rgrid, dim3(64), 0, st, p);
-    if (p.ndense != 0)
-      hipLaunchKernelGGL((m2_dense_read_kernel<DK, DV, AT, UT, WMAX>),
-                         dim3(p.B * (p.ndense > 0 ? p.ndense : p.H)), dim3(64), 0, st, p);
+    if (p.ndense > 0)
+      hipLaunchKernelGGL((m2_dense_read_kernel<DK, DV, AT, UT, WMAX>), dim3(p.B * p.ndense), dim3(64), 0,
+                         st, p);
   } else {
     hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF>), dim3(dn_read_blocks(p.B, p.H)),
                        dim3(64 * DN_TPW), 0, st, p);

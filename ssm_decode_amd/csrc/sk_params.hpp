@@ -31,9 +31,8 @@ struct Params {
   void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
   void* Cs;             // state-dependent coefficient maps [B][R][dk] sketch dtype
   void* Sc;             // state copies of dense-fallback heads [B][H][dk][dv] sketch dtype
-  int ndense;           // dense-fallback heads: 0 none; > 0 their count, listed in dense_list;
-                        // -1 more than DENSE_LIST_MAX (kernels check every head)
-  int16_t dense_list[DENSE_LIST_MAX];
+  int ndense;           // dense-fallback heads, in head order in dense_list; their state
+  int16_t dense_list[DENSE_LIST_MAX];  // copies are Sc[b][position in the list]
   float ridge;          // relative ridge of the state-dependent map
   const void* q;
   const void* k;
@@ -54,6 +53,13 @@ struct M2Work {
     total = n0 + ((size_t)B * G + 63) / 64 * 64;
   }
 };
+
+// Position of dense-fallback head h in the list (h must be listed).
+__host__ __device__ inline int dense_slot(const Params& p, int h) {
+  int k = 0;
+  while (k + 1 < p.ndense && p.dense_list[k] != h) ++k;
+  return k;
+}
 
 // Launch one kernel of `family` for `mode`; returns 0, or -2 when the shape
 // / dtype combination has no instantiation, or -5 on a launch error.

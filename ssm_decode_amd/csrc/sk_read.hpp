@@ -410,10 +410,10 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   static_assert(LPRW >= 1 && LPRW <= 64 && DK % RPP == 0, "state copy split into lane chunks");
   __shared__ float s_q[DK];
   const int lane = threadIdx.x;
-  const int nd = p.ndense > 0 ? p.ndense : p.H;     // a list of dense heads, or every head
+  const int nd = p.ndense;
   const int b = blockIdx.x / nd;
-  const int h = p.ndense > 0 ? p.dense_list[blockIdx.x - b * nd] : blockIdx.x - b * nd;
-  if (p.off[h + 1] != p.off[h]) return;             // (every-head grid) a sketched head
+  const int slot = blockIdx.x - b * nd;              // position in the dense list
+  const int h = p.dense_list[slot];
   const int W = p.W;
   const int g = h / p.HPG;
   const size_t bg = (size_t)b * p.G + g, bh = (size_t)b * p.H + h;
@@ -426,7 +426,7 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
 
   // loads: the state copy, the query, the slot gates and dot products, the
   // ring values and the step's own value
-  const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + cc * CE;
+  const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + ((size_t)b * nd + slot) * DK * DV + cc * CE;
   VecN<UT, CE> sr[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) sr[i] = ldraw<CE>(Sr + (size_t)(r0 + RPP * i) * DV);
@@ -687,7 +687,8 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
     if (rk == 0) {
       // dense-fallback head: out += Scopy^T r, 16 rows at a time, each r_m
       // read from the lane that holds it
-      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + bh * DK * DV + lv;
+      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) +
+                     ((size_t)bcl * p.ndense + dense_slot(p, h)) * DK * DV + lv;
 #pragma unroll 1
       for (int m0 = 0; m0 < DK; m0 += 16) {
         VecN<UT, EV> sr[16];

@@ -282,7 +282,7 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
 
 // (the delta-rule flush runs three waves per SIMD: its chunked update has
 // serial phases that more resident tiles hide)
-template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX, int COEF>
+template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX, int COEF, bool DENSE>
 __global__ void __launch_bounds__((TileShape<DK, DV>::THREADS), (MODE == MODE_FLUSH && FAM != FAM_M2 ? 3 : 2))
 tile_kernel(Params p) {
   using T = TileShape<DK, DV>;
@@ -889,23 +889,41 @@ tile_kernel(Params p) {
       }
 
     // ------------- dense-fallback head (rank 0): the state copy instead
-    // (stored through a buffer resource: one lane offset instead of a
-    // pointer per row, which would hold registers across the kernel)
-    if (want_u && r == 0) {                        // uniform over the workgroup
-      static_assert(NCC == 2, "the state copy stores two columns per lane");
-      const __amdgpu_buffer_rsrc_t c_rsrc =
-          make_rsrc(reinterpret_cast<UT*>(p.Sc) + bh * DK * DV, DK * DV * (int)sizeof(UT));
-      const int c_lane = (4 * rg * DV + colbase) * (int)sizeof(UT);
+    // Each wave holds only its column block of a row, so direct stores
+    // would write every row in partial lines from several waves (measured:
+    // far below the bandwidth of the rest of the flush).  The copy goes
+    // through LDS in bands of RCH rows and leaves as whole rows, 16 bytes a
+    // lane.
+    // (compiled only for layers that have such heads: the branch costs the
+    // kernel registers)
+    if (DENSE && want_u && r == 0) {               // uniform over the workgroup
+      constexpr int RB = DV * (int)sizeof(UT);     // bytes per row of the copy
+      constexpr int FIT = LY::TOTAL * 4 / RB;      // rows that fit in the LDS
+      constexpr int RCH = FIT >= 64 && DK >= 64 ? 64 : FIT >= 32 && DK >= 32 ? 32 : 16;
+      static_assert(RCH <= DK && DK % RCH == 0 && RCH * RB <= LY::TOTAL * 4, "copy bands fit the LDS");
+      static_assert(NCC == 2 && RB % 16 == 0, "the copy is written as pairs and 16-byte chunks");
+      char* s_cp = reinterpret_cast<char*>(smem);
+      UT* Cg = reinterpret_cast<UT*>(p.Sc) + ((size_t)b * p.ndense + dense_slot(p, h)) * DK * DV;
+      __syncthreads();                             // the LDS is no longer read
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int m0 = 0; m0 < DK; m0 += RCH) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float x[2] = {sacc[mb][0][v], sacc[mb][1][v]};
-          buf_st2<UT>(c_rsrc, c_lane, (16 * mb + v) * DV * (int)sizeof(UT), x);
-        }
+        for (int mb = m0 / 16; mb < (m0 + RCH) / 16; ++mb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            UT* dst = reinterpret_cast<UT*>(s_cp + (16 * mb + 4 * rg + v - m0) * RB) + colbase;
+            dst[0] = Store<UT>::cvt(sacc[mb][0][v]);
+            dst[1] = Store<UT>::cvt(sacc[mb][1][v]);
+          }
+        __syncthreads();
+        uint4* gdst = reinterpret_cast<uint4*>(Cg + (size_t)m0 * DV);
+        const uint4* lsrc = reinterpret_cast<const uint4*>(s_cp);
+        for (int c = tid; c < RCH * RB / 16; c += NT) gdst[c] = lsrc[c];
+        __syncthreads();
+      }
     }
     // --------------------------- sketch U = S^T P on the matrix cores
-    if (want_u && r > 0) {
+    if (want_u && (!DENSE || r > 0)) {
       float4 pr[PU];
 #pragma unroll
       for (int u = 0; u < PU; ++u) {

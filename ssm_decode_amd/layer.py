@@ -68,9 +68,10 @@ class DecodeLayer:
         self.Pt = z((self.R, dk), torch.float32)
         self.Cmap = z((self.R, dk), torch.float32)
         self.Cstate = z((B, self.R, dk), ut) if coef == "state" else None
-        # state copies of dense-fallback heads (rank 0), when there are any
-        dense = bool((np.diff(self.offsets_host) == 0).any())
-        self.Scopy = z((B, H, dk, dv), ut) if dense else None
+        # state copies of the dense-fallback heads (rank 0), in head order
+        self.dense_heads = np.nonzero(np.diff(self.offsets_host) == 0)[0]
+        nd = len(self.dense_heads)
+        self.Scopy = z((B, nd, dk, dv), ut) if nd else None
         self.offsets = torch.from_numpy(self.offsets_host.copy()).to(device)
         self.ring_k = z((B, G, W, dk), at)
         self.ring_v = z((B, H, W, dv), at)

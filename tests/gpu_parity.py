@@ -180,8 +180,9 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
                     compare_maps(sel)
                 dense = [ti for ti in sel if li.ranks[tiles[ti, 1]] == 0]
                 if dense:                           # dense-fallback tiles: their state copies
+                    slot = {int(hd): i for i, hd in enumerate(lay.dense_heads)}
                     db = torch.from_numpy(tiles[dense, 0]).to(lay.device)
-                    dh = torch.from_numpy(tiles[dense, 1]).to(lay.device)
+                    dh = torch.tensor([slot[int(tiles[ti, 1])] for ti in dense], device=lay.device)
                     Sc_gpu = lay.Scopy[db, dh].float().cpu().numpy().astype(np.float64)
                     rep.max_Sc = max(rep.max_Sc, rel_l2(Sc_gpu, orc.Sc[dense]))
         if log and (t % 16 == 15 or t == steps - 1):

@@ -209,5 +209,12 @@ def test_dense_fallback_heads(lib):
     Ld = _layer([0, 0, 0, 0, 0], batch=0)            # every head dense: R = 0
     assert _all_calls(Ld, _bufs(U=None, Pt=None, C=None, Cstate=None), _step()) == [0] * 4
     assert abi.sketchssm_workspace_bytes(_layer([0, 0, 0, 0, 0])) == _m2_work_bytes(2, 0, 4, 4)
+    # at most 64 dense heads per layer
+    off = np.concatenate([[0], np.cumsum([0] * 65 + [4] * 63)]).astype(np.int32)
+    assert abi.sketchssm_read(_layer(off, heads=128, groups=128, family=abi.SKSSM_GDN, batch=0),
+                              _bufs(), _step()) == abi.SKSSM_EDIM
+    off = np.concatenate([[0], np.cumsum([0] * 64 + [4] * 64)]).astype(np.int32)
+    assert abi.sketchssm_read(_layer(off, heads=128, groups=128, family=abi.SKSSM_GDN, batch=0),
+                              _bufs(), _step()) == 0
     # with sketched heads the sketch is still required
     assert abi.sketchssm_read(_layer([0, 4, 4, 8, 12]), _bufs(U=None), _step()) == abi.SKSSM_EINVAL
