@@ -394,12 +394,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2894152981,
-                "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
-    "gdn_b256": {"bytes": 1156118148,
-                 "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
-    "kda_b256": {"bytes": 1330910974,
-                 "src_sha256": "66e200783c2c0f6c3f64ccae3e75eb949ccfd6b01bebcdfff992c0e5a0074a8d"},
+    "m2_b320": {"bytes": 2894191176,
+                "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
+    "gdn_b256": {"bytes": 1156127406,
+                 "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
+    "kda_b256": {"bytes": 1330910877,
+                 "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
