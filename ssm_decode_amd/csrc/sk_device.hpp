@@ -76,6 +76,28 @@ __device__ __forceinline__ void ldn(const float* p, float (&x)[N]) {
     }
   }
 }
+// The state's own stream (read once and written once per tile): N = 2 or 4
+// fp32 with the non-temporal cache policy, so that the state passing through
+// does not displace the sketch, ring and inputs the other kernels re-read
+// from the caches.
+template <int N>
+__device__ __forceinline__ void ldn_nt(const float* p, float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "ldn_nt: 2 or 4 floats");
+  typedef float fv __attribute__((ext_vector_type(N)));
+  const fv v = __builtin_nontemporal_load(reinterpret_cast<const fv*>(p));
+#pragma unroll
+  for (int e = 0; e < N; ++e) x[e] = v[e];
+}
+template <int N>
+__device__ __forceinline__ void stn_nt(float* p, const float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "stn_nt: 2 or 4 floats");
+  typedef float fv __attribute__((ext_vector_type(N)));
+  fv v;
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = x[e];
+  __builtin_nontemporal_store(v, reinterpret_cast<fv*>(p));
+}
+
 template <int N>
 __device__ __forceinline__ void ldn(const bf16* p, float (&x)[N]) {
   if constexpr (N == 1) {
@@ -193,29 +215,32 @@ __device__ __forceinline__ void tr_reduce(float (&a)[N], int lane) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-template <int N>
+// Cache policy of the buffer accesses (aux operand): 0 the default, CP_NT
+// non-temporal (the instruction's nt bit on gfx950).
+constexpr int CP_NT = 2;
+template <int N, int CP = 0>
 __device__ __forceinline__ void buf_ld(__amdgpu_buffer_rsrc_t r, int voff, int soff, float (&x)[N]) {
   static_assert(N == 2 || N == 4, "buf_ld: 2 or 4 floats");
   if constexpr (N == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, CP);
     x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
   } else {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
     x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
     x[2] = __uint_as_float(v[2]); x[3] = __uint_as_float(v[3]);
   }
 }
-template <int N>
+template <int N, int CP = 0>
 __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&x)[N]) {
   static_assert(N == 2 || N == 4, "buf_st: 2 or 4 floats");
   if constexpr (N == 2) {
     typedef unsigned int u2 __attribute__((ext_vector_type(2)));
     const u2 v = {__float_as_uint(x[0]), __float_as_uint(x[1])};
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, CP);
   } else {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
     const u4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, CP);
   }
 }
 

@@ -436,9 +436,9 @@ tile_kernel(Params p) {
     for (int v = 0; v < 4; ++v) {
       float x[NCC];
       if constexpr (SBUF)
-        buf_ld<NCC>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+        buf_ld<NCC, CP_NT>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
       else
-        ldn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+        ldn_nt<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
 #pragma unroll
       for (int c = 0; c < NCC; ++c) sacc[mb][c][v] = x[c];
     }
@@ -883,9 +883,9 @@ tile_kernel(Params p) {
 #pragma unroll
         for (int c = 0; c < NCC; ++c) x[c] = sacc[mb][c][v];
         if constexpr (SBUF)
-          buf_st<NCC>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+          buf_st<NCC, CP_NT>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
         else
-          stn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+          stn_nt<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
       }
 
     // ------------- dense-fallback head (rank 0): the state copy instead
