@@ -163,6 +163,35 @@ __device__ __forceinline__ VecN<T, N> ldraw(const T* p) {
 template <typename T, int N>
 __device__ __forceinline__ float vget(const VecN<T, N>& x, int e) { return to_f32(x.v[e]); }
 
+// ldraw with the non-temporal cache policy, for rows a kernel reads once
+// (sketch rows, ring entries, state copies): 2, 4, 8 or a multiple of 16
+// bytes.
+template <int N, typename T>
+__device__ __forceinline__ VecN<T, N> ldraw_nt(const T* p) {
+  constexpr int B = (int)sizeof(T) * N;
+  static_assert(B == 2 || B == 4 || B == 8 || B % 16 == 0, "ldraw_nt: 2, 4, 8 or a multiple of 16 bytes");
+  VecN<T, N> r;
+  if constexpr (B == 2) {
+    const unsigned short v = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+    __builtin_memcpy(&r, &v, 2);
+  } else if constexpr (B == 4) {
+    const unsigned v = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+    __builtin_memcpy(&r, &v, 4);
+  } else if constexpr (B == 8) {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+    __builtin_memcpy(&r, &v, 8);
+  } else {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int o = 0; o < B; o += 16) {
+      const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(reinterpret_cast<const char*>(p) + o));
+      __builtin_memcpy(reinterpret_cast<char*>(&r) + o, &v, 16);
+    }
+  }
+  return r;
+}
+
 // Raw copy of N consecutive elements (ring appends).
 template <int N, typename T>
 __device__ __forceinline__ void copyn(T* dst, const T* src) {

@@ -306,12 +306,12 @@ __global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
     const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < r) us[j] = ldraw<CPL>(Ur + (size_t)j * DV);
+      if (j < r) us[j] = ldraw_nt<CPL>(Ur + (size_t)j * DV);
     VecN<AT, CPL> vs[WMAX];
     const AT* rv0 = ring_v + s * CPL;
 #pragma unroll
     for (int i = 0; i < WMAX - 1; ++i)
-      if (i < n0) vs[i] = ldraw<CPL>(rv0 + (size_t)i * DV);
+      if (i < n0) vs[i] = ldraw_nt<CPL>(rv0 + (size_t)i * DV);
 
     // -------------------------------- decays: suffix products per head
     float dts[SPL], a[SPL], lp = 1.f;
@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + ((size_t)b * nd + slot) * DK * DV + cc * CE;
   VecN<UT, CE> sr[NP];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) sr[i] = ldraw<CE>(Sr + (size_t)(r0 + RPP * i) * DV);
+  for (int i = 0; i < NP; ++i) sr[i] = ldraw_nt<CE>(Sr + (size_t)(r0 + RPP * i) * DV);
   const AT* qg = reinterpret_cast<const AT*>(p.q) + bg * DK;
   for (int m = lane; m < DK; m += 64) s_q[m] = ld(qg + m);
   const AT* ring_dt = reinterpret_cast<const AT*>(p.rg) + bh * W;
@@ -440,7 +440,7 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   VecN<AT, CE> vs[WMAX];
 #pragma unroll
   for (int i = 0; i < WMAX - 1; ++i)
-    if (i < n0) vs[i] = ldraw<CE>(ring_v + (size_t)i * DV);
+    if (i < n0) vs[i] = ldraw_nt<CE>(ring_v + (size_t)i * DV);
   const VecN<AT, CE> vcur = ldraw<CE>(reinterpret_cast<const AT*>(p.v) + bh * DV + cc * CE);
 
   // decays: a_i = exp(-dt_i e^A), w_i = dt_i prod_{t>i} a_t, D = prod_t a_t
@@ -590,8 +590,8 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
 #pragma unroll
   for (int i = 0; i < WMAX - 1; ++i) {
     if (i < nr) {                                // uniform
-      ks[i] = ldraw<EK>(ring_k + (size_t)i * DK);
-      vs[i] = ldraw<EV>(ring_v + (size_t)i * DV);
+      ks[i] = ldraw_nt<EK>(ring_k + (size_t)i * DK);
+      vs[i] = ldraw_nt<EV>(ring_v + (size_t)i * DV);
       if (FAM == FAM_KDA) ldn<KG>(ring_g + (size_t)i * DK, gs[i]);
     }
   }
@@ -610,7 +610,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)bcl * p.R + off) * DV + lv;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (j < rk && rd) us[j] = ldraw<EV>(Ur + (size_t)j * DV);
+    if (j < rk && rd) us[j] = ldraw_nt<EV>(Ur + (size_t)j * DV);
 
   if constexpr (!COEF) {
     // (every load is in flight before the wait for the staged rows)
@@ -693,7 +693,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
       for (int m0 = 0; m0 < DK; m0 += 16) {
         VecN<UT, EV> sr[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sr[j] = ldraw<EV>(Sr + (size_t)(m0 + j) * DV);
+        for (int j = 0; j < 16; ++j) sr[j] = ldraw_nt<EV>(Sr + (size_t)(m0 + j) * DV);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float rm = lane_value(r[j % EK], (m0 + j) / EK);
