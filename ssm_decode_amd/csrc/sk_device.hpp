@@ -88,6 +88,12 @@ __device__ __forceinline__ void ldn_nt(const float* p, float (&x)[N]) {
 #pragma unroll
   for (int e = 0; e < N; ++e) x[e] = v[e];
 }
+// 16 bytes with the non-temporal cache policy.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 template <int N>
 __device__ __forceinline__ void stn_nt(float* p, const float (&x)[N]) {
   static_assert(N == 2 || N == 4, "stn_nt: 2 or 4 floats");

@@ -362,7 +362,9 @@ tile_kernel(Params p) {
       sc_beta = (has_in && i == n0) ? p.beta[bh] : p.rb[bh * W + i];
     }
   }
-  // keys: n rows of DK
+  // keys: n rows of DK (a Mamba-2 key is shared by the group's heads and
+  // stays cacheable; every other ring entry is read by this tile only, with
+  // the non-temporal policy)
   constexpr int KC = Chunk<AT>::N;
   constexpr int KCPR = DK / KC;
   constexpr int KU = cdiv(WMAX * KCPR, NT);
@@ -372,7 +374,7 @@ tile_kernel(Params p) {
     const int c = tid + NT * u;
     if (c < n * KCPR) {
       const int i = c / KCPR, m0 = (c - i * KCPR) * KC;
-      kr[u] = *reinterpret_cast<const uint4*>(key_ptr(i) + m0);
+      kr[u] = FAM == FAM_M2 ? *reinterpret_cast<const uint4*>(key_ptr(i) + m0) : ld16_nt(key_ptr(i) + m0);
     }
   }
   // values: n rows of DV
@@ -384,7 +386,7 @@ tile_kernel(Params p) {
     const int c = tid + NT * u;
     if (c < n * VCPR) {
       const int i = c / VCPR, c0 = (c - i * VCPR) * KC;
-      vr[u] = *reinterpret_cast<const uint4*>(val_ptr(i) + c0);
+      vr[u] = ld16_nt(val_ptr(i) + c0);
     }
   }
   // KDA gates: n rows of DK fp32
@@ -397,7 +399,8 @@ tile_kernel(Params p) {
       const int c = tid + NT * u;
       if (c < n * GCPR) {
         const int i = c / GCPR, m0 = (c - i * GCPR) * 4;
-        gr[u] = *reinterpret_cast<const float4*>(gate_vec(i) + m0);
+        const uint4 t = ld16_nt(gate_vec(i) + m0);
+        gr[u] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z), __uint_as_float(t.w));
       }
     }
   }
