@@ -39,7 +39,7 @@ static void launch_read(const Params& p, hipStream_t st) {
     const dim3 pgrid(PrepGrid<COEF, DK, UT>::blocks(p.B), p.G);
     const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
     hipLaunchKernelGGL((m2_prep_kernel<DK, AT, UT, WMAX, COEF>), pgrid, dim3(CQ_THREADS), 0, st, p);
-    hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, WMAX>), rgrid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, WMAX>), rgrid, dim3(64 * M2R_WPB), 0, st, p);
     if (p.ndense > 0)
       hipLaunchKernelGGL((m2_dense_read_kernel<DK, DV, AT, UT, WMAX>), dim3(p.B * p.ndense), dim3(64), 0,
                          st, p);

@@ -225,8 +225,9 @@ __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
   *reinterpret_cast<VecN<T, N>*>(p) = x;
 }
 
-// Sketched read: one wave per (sequence, group, block of M2R_HPW heads), 16
-// lanes per head (one DPP row).  Lane s of a head holds ring slots s*SPL..
+// Sketched read: one wave per (sequence, group, block of M2R_HPW heads),
+// M2R_WPB consecutive such waves a workgroup, 16 lanes per head (one DPP
+// row).  Lane s of a head holds ring slots s*SPL..
 // for the decay scan, coefficient j = s, and output columns s*CPL.. .  The
 // ring fill comes from the prep kernel's workspace; then every load is
 // issued before the first wait: slot gates and dot products, the head's cq
@@ -237,27 +238,31 @@ __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
 // lanes wrote).
 constexpr int M2R_LPH = 16;        // lanes per head
 constexpr int M2R_HPW = 64 / M2R_LPH;   // heads per wave
+constexpr int M2R_WPB = 4;         // waves per workgroup (measured: 1, 2, 4, 8, 16 -> 4 best)
 
-inline int m2_read_blocks(int B, int G, int HPG) {
-  return B * G * ((HPG + M2R_HPW - 1) / M2R_HPW);
-}
+__host__ __device__ inline int m2_read_items(int B, int G, int HPG) { return B * G * ((HPG + M2R_HPW - 1) / M2R_HPW); }
+inline int m2_read_blocks(int B, int G, int HPG) { return (m2_read_items(B, G, HPG) + M2R_WPB - 1) / M2R_WPB; }
 
 template <int DK, int DV, typename AT, typename UT, int WMAX>
-__global__ void __launch_bounds__(64) m2_read_kernel(Params p) {
+__global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
   constexpr int LPH = M2R_LPH;
   constexpr int HPW = M2R_HPW;
   constexpr int SEG = DK / LPH;                  // key elements per lane (append)
   constexpr int CPL = DV / LPH;                  // output columns per lane
   constexpr int SPL = WMAX / LPH;                // ring slots per lane in the decay scan
   static_assert(SEG >= 1 && CPL >= 1 && SPL >= 1, "head dims too small for the lane split");
-  __shared__ __align__(16) float s_e[HPW * WMAX];  // w_i d_i per head
-  __shared__ __align__(16) float s_c[HPW * 16];    // cq entries per head
+  __shared__ __align__(16) float s_e_wg[M2R_WPB][HPW * WMAX];  // w_i d_i per head
+  __shared__ __align__(16) float s_c_wg[M2R_WPB][HPW * 16];    // cq entries per head
+  float* s_e = s_e_wg[threadIdx.x >> 6];           // this wave's part
+  float* s_c = s_c_wg[threadIdx.x >> 6];
 
   const int wpg = (p.HPG + HPW - 1) / HPW;
-  const int item = blockIdx.x;
+  // consecutive waves of a workgroup: the head blocks of one (sequence, group)
+  const int item = blockIdx.x * M2R_WPB + (threadIdx.x >> 6);
+  if (item >= m2_read_items(p.B, p.G, p.HPG)) return;
   const int bgi = item / wpg;
   const int wq = item - bgi * wpg;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 63;
   const int hh = tid >> 4;                       // head row of the wave
   const int s = tid & 15;
   const int W = p.W, HPG = p.HPG;
