@@ -394,12 +394,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2894191176,
-                "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
-    "gdn_b256": {"bytes": 1156127406,
-                 "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
-    "kda_b256": {"bytes": 1330910877,
-                 "src_sha256": "fa119815e3e9f83120534c16a13a7cdf662391b99417884ab9fd44ca5fd9b73a"},
+    "m2_b320": {"bytes": 2891451676,
+                "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
+    "gdn_b256": {"bytes": 1155965569,
+                 "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
+    "kda_b256": {"bytes": 1213752728,
+                 "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 

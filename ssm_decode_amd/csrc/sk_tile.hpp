@@ -430,6 +430,11 @@ tile_kernel(Params p) {
   // plain pointers elsewhere (the Mamba-2 kernels run best at their current
   // occupancy).
   constexpr bool SBUF = STATE_BUFFER<FAM, MODE>::value;
+  // Cache policy of the state stream: non-temporal where every step of the
+  // mode reads and writes the whole state once (flush, standard step); the
+  // ReplaySSM step, which re-reads the state at every step and writes it
+  // once a window, is measured faster with the default policy.
+  constexpr int S_CP = MODE == MODE_REPLAY ? 0 : CP_NT;
   const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.S + bh * DK * DV, DK * DV * 4);
   const int s_lane = (4 * rg * DV + colbase) * 4;
   f32x4v sacc[MB][NCC];
@@ -439,9 +444,11 @@ tile_kernel(Params p) {
     for (int v = 0; v < 4; ++v) {
       float x[NCC];
       if constexpr (SBUF)
-        buf_ld<NCC, CP_NT>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
-      else
+        buf_ld<NCC, S_CP>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+      else if constexpr (S_CP == CP_NT)
         ldn_nt<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+      else
+        ldn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
 #pragma unroll
       for (int c = 0; c < NCC; ++c) sacc[mb][c][v] = x[c];
     }
@@ -886,9 +893,11 @@ tile_kernel(Params p) {
 #pragma unroll
         for (int c = 0; c < NCC; ++c) x[c] = sacc[mb][c][v];
         if constexpr (SBUF)
-          buf_st<NCC, CP_NT>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
-        else
+          buf_st<NCC, S_CP>(s_rsrc, s_lane, (16 * mb + v) * DV * 4, x);
+        else if constexpr (S_CP == CP_NT)
           stn_nt<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
+        else
+          stn<NCC>(p.S + bh * DK * DV + colbase + (size_t)(16 * mb + 4 * rg + v) * DV, x);
       }
 
     // ------------- dense-fallback head (rank 0): the state copy instead
