@@ -161,8 +161,8 @@ typedef struct {             /* one decode step */
  * (a dense-fallback head: o = Scopy^T q~ + o_buf), otherwise leave o for
  * sketchssm_flush.  Never reads S.  C is bufs->C
  * (SKSSM_COEF_FIXED) or the tile's own map in bufs->Cstate, as its last
- * flush wrote it (SKSSM_COEF_STATE).  Mamba-2 layers need bufs->work
- * (sketchssm_workspace_bytes). */
+ * flush wrote it (SKSSM_COEF_STATE).  Mamba-2 layers, and GDN/KDA layers
+ * with dense-fallback heads, need bufs->work (sketchssm_workspace_bytes). */
 int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                    const sketchssm_step* step, void* hip_stream);
 
@@ -202,8 +202,11 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
  * query's coordinates in every head's sketch basis, C_h q (B x R fp32; the
  * decay factor of the pulled-back query is applied afterwards), the dot
  * products of the query with the group's buffered keys (B x G x W fp32) and
- * the group's checked ring fill (B x G int32).  The caller allocates it; the
- * library never does. */
+ * the group's checked ring fill (B x G int32).  GDN and KDA use it only when
+ * the layer has dense-fallback heads: per (sequence, dense head) the
+ * pulled-back query (dk fp32), the buffered term (dv fp32) and a flag
+ * (int32), passed from the read's main launch to the launch that reads the
+ * state copies.  The caller allocates it; the library never does. */
 int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
 
 /* Library version (major * 10000 + minor * 100 + patch). */

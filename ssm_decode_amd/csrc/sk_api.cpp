@@ -35,10 +35,18 @@ bool any_dense(const sketchssm_layer* L) {
   return false;
 }
 
-// Workspace of a Mamba-2 read (layout in sk_params.hpp): the query in every
-// head's basis, the key-query dot products and the checked ring fill.
+// Workspace of a read (layouts in sk_params.hpp).  Mamba-2: the query in
+// every head's basis, the key-query dot products and the checked ring fill.
+// GDN/KDA: only with dense-fallback heads, the pulled-back query and the
+// buffered term of each such tile, for the launch that reads the copies.
 int64_t workspace_bytes(const sketchssm_layer* L) {
-  if (L->family != SKSSM_MAMBA2) return 0;
+  if (L->family != SKSSM_MAMBA2) {
+    int nd = 0;
+    for (int h = 0; h < L->heads; ++h) nd += L->rank_offsets_host[h + 1] == L->rank_offsets_host[h];
+    if (nd == 0) return 0;
+    const sk::DnWork w(L->batch, nd, L->dk, L->dv);
+    return (int64_t)w.total * 4;
+  }
   const sk::M2Work w(L->batch, L->rank_offsets_host[L->heads], L->qk_groups, L->window);
   return (int64_t)w.total * 4;
 }

@@ -28,7 +28,7 @@ struct Params {
   int32_t* count;
   const float* A;
   int32_t* err;
-  void* work;           // workspace (Mamba-2 read: cq [B][R] fp32)
+  void* work;           // workspace (Mamba-2 read: M2Work; GDN/KDA read with dense heads: DnWork)
   void* Cs;             // state-dependent coefficient maps [B][R][dk] sketch dtype
   void* Sc;             // state copies of dense-fallback heads [B][H][dk][dv] sketch dtype
   int ndense;           // dense-fallback heads, in head order in dense_list; their state
@@ -51,6 +51,20 @@ struct M2Work {
     d = cq;
     n0 = d + ((size_t)B * G * W + 63) / 64 * 64;
     total = n0 + ((size_t)B * G + 63) / 64 * 64;
+  }
+};
+
+// Workspace of a GDN/KDA read with dense-fallback heads (floats): per
+// (sequence, dense head) the pulled-back query r [B][D][DK], the buffered
+// term [B][D][DV] and a flag [B][D] (int32, 1 when the step has an output),
+// each region 256-byte aligned.
+struct DnWork {
+  size_t r, ob, flag, total;
+  __host__ __device__ DnWork(int B, int D, int DK, int DV) {
+    r = 0;
+    ob = ((size_t)B * D * DK + 63) / 64 * 64;
+    flag = ob + ((size_t)B * D * DV + 63) / 64 * 64;
+    total = flag + ((size_t)B * D + 63) / 64 * 64;
   }
 };
 

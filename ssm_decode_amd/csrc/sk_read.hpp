@@ -628,6 +628,11 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
     }
     __syncthreads();
   }
+  if (active && rk == 0 && lane == 0) {          // whether the dense launch writes o
+    const DnWork wl(p.B, p.ndense, DK, DV);
+    reinterpret_cast<int*>(reinterpret_cast<float*>(p.work) + wl.flag)[(size_t)bcl * p.ndense + dense_slot(p, h)] =
+        rd ? 1 : 0;
+  }
   if (!active) return;
   if (!ok) {
     if (lane == 0) atomicOr(p.err, ERRBIT_COUNT);
@@ -690,24 +695,17 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
       }
     }
     if (rk == 0) {
-      // dense-fallback head: out += Scopy^T r, 16 rows at a time, each r_m
-      // read from the lane that holds it
-      const UT* Sr = reinterpret_cast<const UT*>(p.Sc) +
-                     ((size_t)bcl * p.ndense + dense_slot(p, h)) * DK * DV + lv;
-#pragma unroll 1
-      for (int m0 = 0; m0 < DK; m0 += 16) {
-        VecN<UT, EV> sr[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sr[j] = ldraw_nt<EV>(Sr + (size_t)(m0 + j) * DV);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float rm = lane_value(r[j % EK], (m0 + j) / EK);
-#pragma unroll
-          for (int e = 0; e < EV; ++e) out[e] += rm * vget(sr[j], e);
-        }
-      }
+      // dense-fallback head: the pulled-back query and the buffered term go
+      // to the workspace, and dn_dense_read_kernel adds Scopy^T r and
+      // writes o
+      const DnWork wl(p.B, p.ndense, DK, DV);
+      const size_t t = (size_t)bcl * p.ndense + dense_slot(p, h);
+      float* ws = reinterpret_cast<float*>(p.work);
+      if (kl) stn<EK>(ws + wl.r + t * DK + lk, r);
+      if (vl) stn<EV>(ws + wl.ob + t * DV + lv, out);
+    } else if (vl) {
+      stn<EV>(reinterpret_cast<AT*>(p.o) + bh * DV + lv, out);
     }
-    if (vl) stn<EV>(reinterpret_cast<AT*>(p.o) + bh * DV + lv, out);
   }
 
   // ------------------------------------------------------------ append
@@ -721,6 +719,63 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   if (lane == 0) {
     ring_b[n0] = bcur;
     p.count[bh] = n;
+  }
+}
+
+// Dense-fallback heads of a GDN/KDA layer at a non-flush step: one
+// workgroup per (sequence, dense head), launched after dn_read_kernel, which
+// leaves the tile's pulled-back query r and buffered term in the workspace
+// with a flag set when the step has an output:  o = Scopy^T r + o_buf.
+// Every 16-byte chunk of the state copy is in flight at once: thread t takes
+// chunk t % LPRW of rows t / LPRW + RPP i, and the partial sums of a chunk
+// column are added through LDS.
+constexpr int DND_THREADS = 256;
+
+template <int DK, int DV, typename AT, typename UT>
+__global__ void __launch_bounds__(DND_THREADS) dn_dense_read_kernel(Params p) {
+  constexpr int CE = 16 / (int)sizeof(UT);           // elements per chunk
+  constexpr int LPRW = DV / CE;                      // threads per row
+  constexpr int RPP0 = DND_THREADS / LPRW;
+  constexpr int RPP = RPP0 < DK ? RPP0 : DK;         // rows per pass
+  constexpr int NP = DK / RPP;                       // passes
+  static_assert(LPRW >= 1 && LPRW <= DND_THREADS && DK % RPP == 0, "state copy split into chunks");
+  __shared__ float s_r[DK];
+  __shared__ float s_part[RPP][DV];
+  const int tid = threadIdx.x;
+  const int nd = p.ndense;
+  const int b = blockIdx.x / nd;
+  const int slot = blockIdx.x - b * nd;              // position in the dense list
+  const int h = p.dense_list[slot];
+  const size_t t = (size_t)b * nd + slot;
+  const DnWork wl(p.B, nd, DK, DV);
+  const float* ws = reinterpret_cast<const float*>(p.work);
+  if (reinterpret_cast<const int*>(ws + wl.flag)[t] == 0) return;   // no output this step (uniform)
+  const bool on = tid < RPP * LPRW;
+  const int cc = tid % LPRW, r0 = on ? tid / LPRW : 0;
+  const UT* Sr = reinterpret_cast<const UT*>(p.Sc) + t * DK * DV + cc * CE;
+  VecN<UT, CE> sr[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) sr[i] = ldraw_nt<CE>(Sr + (size_t)(r0 + RPP * i) * DV);
+  if (tid < DK) s_r[tid] = ws[wl.r + t * DK + tid];
+  __syncthreads();
+  float acc[CE];
+#pragma unroll
+  for (int c = 0; c < CE; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const float rm = s_r[r0 + RPP * i];
+#pragma unroll
+    for (int c = 0; c < CE; ++c) acc[c] += rm * vget(sr[i], c);
+  }
+  if (on)
+#pragma unroll
+    for (int c = 0; c < CE; ++c) s_part[r0][cc * CE + c] = acc[c];
+  __syncthreads();
+  if (tid < DV) {
+    float o = ws[wl.ob + t * DV + tid];
+#pragma unroll
+    for (int g = 0; g < RPP; ++g) o += s_part[g][tid];
+    st(reinterpret_cast<AT*>(p.o) + ((size_t)b * p.H + h) * DV + tid, o);
   }
 }
 

@@ -160,6 +160,27 @@ def test_workspace_bytes(lib):
     assert abi.sketchssm_workspace_bytes(None) == abi.SKSSM_EINVAL
 
 
+def _dn_work_bytes(B, D, dk, dv):
+    # per (sequence, dense head) the pulled-back query [B][D][dk], the
+    # buffered term [B][D][dv] and a flag [B][D], 4 bytes each, every region
+    # rounded up to 256 bytes
+    a64 = lambda n: (n + 63) // 64 * 64
+    return 4 * (a64(B * D * dk) + a64(B * D * dv) + a64(B * D))
+
+
+def test_workspace_bytes_delta_rule_dense_heads(lib):
+    """GDN/KDA layers need a workspace only when they have dense-fallback
+    heads, and then the read requires it."""
+    for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
+        L = _layer([0, 4, 4, 8, 8], family=fam, batch=3)          # heads 1 and 3 dense
+        assert abi.sketchssm_workspace_bytes(L) == _dn_work_bytes(3, 2, 16, 32) == 1536
+        assert abi.sketchssm_read(L, _bufs(work=None), _step()) == abi.SKSSM_EINVAL
+        assert abi.sketchssm_read(L, _bufs(work=FAKE + 4), _step()) == abi.SKSSM_EINVAL
+        off = np.concatenate([[0], np.cumsum([0] + [8] * 31)]).astype(np.int32)
+        L = _layer(off, family=fam, batch=256, heads=32, groups=32, dk=128, dv=128, W=16)
+        assert abi.sketchssm_workspace_bytes(L) == _dn_work_bytes(256, 1, 128, 128)
+
+
 def test_read_needs_its_workspace(lib):
     L = _layer(OK_OFF)
     assert abi.sketchssm_read(L, _bufs(work=None), _step()) == abi.SKSSM_EINVAL
