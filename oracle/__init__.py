@@ -24,6 +24,7 @@ _LIB = os.path.join(_HERE, "_build", "libsketchssm_oracle.so")
 FAMILY = {"mamba2": 0, "gdn": 1, "kda": 2}
 STORE = {"exact": 0, "f32": 1, "bf16": 2}
 COEF = {"fixed": 0, "state": 1}
+PULLBACK = {"serial": 0, "wy": 1}
 ERR_COUNT = 1
 
 
@@ -41,7 +42,8 @@ def build(force: bool = True) -> str:
 class _Layer(C.Structure):
     _fields_ = [("family", C.c_int), ("dk", C.c_int), ("dv", C.c_int), ("W", C.c_int),
                 ("rmax", C.c_int), ("state_store", C.c_int), ("sketch_store", C.c_int),
-                ("out_store", C.c_int), ("coef_mode", C.c_int), ("coef_ridge", C.c_double)]
+                ("out_store", C.c_int), ("coef_mode", C.c_int), ("coef_ridge", C.c_double),
+                ("pullback", C.c_int)]
 
 
 _DP = C.POINTER(C.c_double)
@@ -110,6 +112,9 @@ class OracleLayer:
     coef: "fixed" reads the per-head table Cmap; "state" makes every flush
     write each tile's own map from its new state (Cmap is then ignored) with
     the relative ridge ``ridge``; the map is stored in the sketch dtype.
+    pullback: how the sketched read evaluates the effective query and the
+    buffered term, "serial" (one transition at a time) or "wy" (every slot's
+    coefficient at once from a triangular system, paper App. C.1).
     """
 
     def __init__(self, family: str, dk: int, dv: int, W: int, ranks: np.ndarray,
@@ -117,7 +122,7 @@ class OracleLayer:
                  A: Optional[np.ndarray], tiles: np.ndarray, S0: np.ndarray,
                  heads: int, qk_groups: int, state_store="f32", sketch_store="f32",
                  out_store="f32", count0: Optional[np.ndarray] = None,
-                 coef: str = "fixed", ridge: float = 0.0):
+                 coef: str = "fixed", ridge: float = 0.0, pullback: str = "serial"):
         self.family, self.dk, self.dv, self.W = family, dk, dv, W
         self.tiles = np.ascontiguousarray(np.asarray(tiles, dtype=np.int64).reshape(-1, 2))
         n = len(self.tiles)
@@ -147,7 +152,8 @@ class OracleLayer:
         self.count = np.zeros(n, dtype=np.int32) if count0 is None else \
             np.ascontiguousarray(np.asarray(count0, dtype=np.int32).reshape(n)).copy()
         self.L = _Layer(FAMILY[family], dk, dv, W, self.rmax, STORE[state_store],
-                        STORE[sketch_store], STORE[out_store], COEF[coef], float(ridge))
+                        STORE[sketch_store], STORE[out_store], COEF[coef], float(ridge),
+                        PULLBACK[pullback])
 
     # ------------------------------------------------------------------
     def _tiles_struct(self):

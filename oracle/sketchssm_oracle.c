@@ -28,7 +28,12 @@
  *    fixed-coefficient rule, App. G) or, as the project page's per-window
  *    flush panel has it, the state-dependent map C = (U^T U)^+ U^T S0^T
  *    refreshed at every flush (paper App. A.2.1; App. A.2.2 names the
- *    regularised solve that is written out here).
+ *    regularised solve that is written out here);
+ *  - the effective query and the buffered term can be evaluated either
+ *    serially, one buffered transition at a time, or all at once from a
+ *    triangular system over the buffered slots (paper App. C.1, the
+ *    WY-style parallel evaluation; the system below is this oracle's
+ *    written-out reading of it).
  *
  * Per family (the Mamba-2 write term, the KDA operator order and the gate
  * dtypes are readings taken where the pages leave the step open):
@@ -53,6 +58,7 @@ enum { ORC_MAMBA2 = 0, ORC_GDN = 1, ORC_KDA = 2 };
 enum { ORC_STORE_EXACT = 0, ORC_STORE_F32 = 1, ORC_STORE_BF16 = 2 };
 enum { ORC_OK = 0, ORC_ERR_COUNT = 1 };
 enum { ORC_COEF_FIXED = 0, ORC_COEF_STATE = 1 };
+enum { ORC_PULLBACK_SERIAL = 0, ORC_PULLBACK_WY = 1 };
 
 typedef struct {
     int family;
@@ -64,6 +70,7 @@ typedef struct {
     int coef_mode;     /* ORC_COEF_FIXED: C is an input table;
                           ORC_COEF_STATE: the flush writes C from the new state */
     double coef_ridge; /* ORC_COEF_STATE: ridge relative to the mean Gram eigenvalue */
+    int pullback;      /* the sketched read's effective query: ORC_PULLBACK_SERIAL or _WY */
 } orc_layer;
 
 /* n independent tiles; every array is indexed by tile first. */
@@ -243,6 +250,72 @@ static void effective_query(const orc_layer* L, const orc_tiles* T, int i, int n
         for (int j = 0; j < L->dv; ++j) obuf[j] += w * v[j];
         pull_back(L, A, r, k, g, beta);
     }
+}
+
+/* Decay of buffered slot p at key element m: Mamba-2 a_p, GDN alpha_p,
+ * KDA g_p[m]. */
+static double slot_decay(const orc_layer* L, const orc_tiles* T, int i, int p, int m) {
+    const double* g = RG(T, L, i, p);
+    if (L->family == ORC_MAMBA2) return m2_decay(g[0], tile_A(T, i));
+    return L->family == ORC_KDA ? g[m] : g[0];
+}
+
+/* The same q~ and o_buf as effective_query, with every buffered slot's
+ * coefficient found at once (paper App. C.1).  Slots 0..n-1, oldest first.
+ * Write D(j,l) = prod_{p=j+1..l} of the slot decays (elementwise for KDA;
+ * the empty product is 1) and e = 1 for the erase terms of GDN/KDA (0 for
+ * Mamba-2).  The serial form's coefficients d_j = k_j . r_j, r_j the query
+ * pulled back through the slots newer than j, satisfy
+ *     d_j + sum_{l>j} e beta_l <k_j, D(j,l) k_l> d_l = <k_j, D(j,n-1) q>,
+ * an upper-triangular system solved by back substitution; then
+ *     q~    = D(-1,n-1) q - sum_l e beta_l d_l D(-1,l) k_l,
+ *     o_buf = sum_l s_l d_l v_l   (s_l the slot's write scale). */
+static void effective_query_wy(const orc_layer* L, const orc_tiles* T, int i, int n,
+                               const double* q, double* r, double* obuf) {
+    const int dk = L->dk;
+    const int erase = L->family != ORC_MAMBA2;
+    double* Lm = (double*)calloc((size_t)(n > 0 ? n : 1) * (n > 0 ? n : 1), sizeof(double));
+    double* b = (double*)calloc(n > 0 ? n : 1, sizeof(double));
+    double* d = (double*)calloc(n > 0 ? n : 1, sizeof(double));
+    double* D = (double*)malloc(sizeof(double) * dk);
+    for (int j = 0; j < n; ++j) {
+        const double* kj = RK(T, L, i, j);
+        for (int m = 0; m < dk; ++m) D[m] = (g_mutation == 15) ? slot_decay(L, T, i, j, m) : 1.0;
+        for (int l = j + 1; l < n; ++l) {          /* D = D(j, l) */
+            const double* kl = RK(T, L, i, l);
+            double t = 0.0;
+            for (int m = 0; m < dk; ++m) {
+                D[m] *= slot_decay(L, T, i, l, m);
+                t += kj[m] * D[m] * kl[m];
+            }
+            if (erase) Lm[(size_t)j * n + l] = RB(T, L, i, l) * t;
+        }
+        double t = 0.0;                              /* D = D(j, n-1) */
+        for (int m = 0; m < dk; ++m) t += kj[m] * D[m] * q[m];
+        b[j] = t;
+    }
+    for (int j = n - 1; j >= 0; --j) {
+        double t = b[j];
+        for (int l = j + 1; l < n; ++l) t -= Lm[(size_t)j * n + l] * d[l];
+        d[j] = t;
+    }
+    for (int m = 0; m < dk; ++m) { D[m] = 1.0; r[m] = 0.0; }
+    for (int l = 0; l < n; ++l) {                    /* D = D(-1, l) */
+        const double* kl = RK(T, L, i, l);
+        const double wl = erase ? RB(T, L, i, l) * d[l] : 0.0;
+        for (int m = 0; m < dk; ++m) {
+            D[m] *= slot_decay(L, T, i, l, m);
+            r[m] -= wl * D[m] * kl[m];
+        }
+    }
+    for (int m = 0; m < dk; ++m) r[m] += D[m] * q[m];
+    for (int j = 0; j < L->dv; ++j) obuf[j] = 0.0;
+    for (int l = 0; l < n; ++l) {
+        const double w = write_scale(L, RG(T, L, i, l), RB(T, L, i, l)) * d[l];
+        const double* v = RV(T, L, i, l);
+        for (int j = 0; j < L->dv; ++j) obuf[j] += w * v[j];
+    }
+    free(Lm); free(b); free(d); free(D);
 }
 
 /* Apply ring entries 0..n-1 in order to the fp64 copy S of the stored state. */
@@ -428,7 +501,10 @@ int orc_read(const orc_layer* L, orc_tiles* T, const orc_step* st) {
         double* c = (double*)malloc(sizeof(double) * (r > 0 ? r : 1));
         double* o = (double*)malloc(sizeof(double) * L->dv);
         const double* q = st->q + (size_t)i * L->dk;
-        effective_query(L, T, i, n, q, qt, obuf);
+        if (L->pullback == ORC_PULLBACK_WY)
+            effective_query_wy(L, T, i, n, q, qt, obuf);
+        else
+            effective_query(L, T, i, n, q, qt, obuf);
         const double* C = TC(T, L, i);
         const double* U = TU(T, L, i);
         for (int j = 0; j < r; ++j)   /* c = C q~ */
@@ -486,7 +562,7 @@ int orc_replay_step(const orc_layer* L, orc_tiles* T, const orc_step* st) {
     return err;
 }
 
-int orc_abi_version(void) { return 2; }
+int orc_abi_version(void) { return 3; }
 
 #ifdef _OPENMP
 #include <omp.h>

@@ -9,7 +9,7 @@ import oracle
 
 
 def single_tile(family, dk, dv, W, S0, Pt, Cm, A=0.0, store="exact", count0=0,
-                coef="fixed", ridge=0.0, sketch_store=None):
+                coef="fixed", ridge=0.0, sketch_store=None, pullback="serial"):
     """An OracleLayer with one (sequence, head) tile; Pt, Cm: [r][dk]."""
     r = Pt.shape[0]
     return oracle.OracleLayer(
@@ -18,7 +18,8 @@ def single_tile(family, dk, dv, W, S0, Pt, Cm, A=0.0, store="exact", count0=0,
         A=None if family != "mamba2" else np.array([A], float),
         tiles=np.array([[0, 0]]), S0=S0[None], heads=1, qk_groups=1,
         state_store=store, sketch_store=store if sketch_store is None else sketch_store,
-        out_store=store, count0=np.array([count0], np.int32), coef=coef, ridge=ridge)
+        out_store=store, count0=np.array([count0], np.int32), coef=coef, ridge=ridge,
+        pullback=pullback)
 
 
 def entry_step(family, e):
