@@ -44,6 +44,8 @@ def parse():
                     help="skip the run with the state-dependent coefficient map")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the run with dense-fallback heads")
+    ap.add_argument("--no-wy", action="store_true",
+                    help="skip the GDN/KDA run with the triangular-system pull-back")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
     ap.add_argument("--cpu-windows", type=int, default=16, help="windows in the CPU sample")
     return ap.parse_args()
@@ -87,11 +89,11 @@ def main():
     feed.fill_state(first, cfg, numpy_all=False)
     S_init = first.S.clone()
 
-    def make_layers(coef, cfg_=None, li_=None):
+    def make_layers(coef, cfg_=None, li_=None, pullback="serial"):
         cfg_, li_ = cfg_ or cfg, li_ or li
         out = []
         for _ in range(L):
-            lay = feed.make_layer(cfg_, li_, device=dev, coef=coef)
+            lay = feed.make_layer(cfg_, li_, device=dev, coef=coef, pullback=pullback)
             lay.S.copy_(S_init)
             assert feed.prime(lay, li_) == 0
             out.append(lay)
@@ -316,6 +318,23 @@ def main():
         log(f"[bench] dense-fallback heads: {dense_block}")
         del layers
 
+    # ------ GDN/KDA: the same workload with the read's effective query from
+    # the triangular system over the buffered slots instead of the serial
+    # pull-back (a Mamba-2 effective query is a decay only: no such run)
+    wy_block = None
+    if not args.no_wy and cfg.family != "mamba2":
+        torch.cuda.empty_cache()
+        layers = make_layers("fixed", pullback="wy")
+        mw = measure(layers)
+        wy_block = {
+            "us_per_step": round(mw["us_per_step"], 3),
+            "achieved_gbs": round(lb.per_step / (mw["us_per_step"] * 1e-6) / 1e9, 1),
+            "flush_us": round(mw["flush_avg"], 2), "read_us": round(mw["read_avg"], 2),
+            "us_per_step_serial": round(us_per_step, 3), "read_us_serial": round(read_avg, 2),
+        }
+        log(f"[bench] triangular-system pull-back: {wy_block}")
+        del layers
+
     # ------------------------------------------ copy-bandwidth reference
     nbytes = 2 * 2 ** 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -383,6 +402,7 @@ def main():
         "sketch_error": approx,
         "state_map": state_map,
         "dense_fallback": dense_block,
+        "wy_pullback": wy_block,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

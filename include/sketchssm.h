@@ -75,6 +75,14 @@ extern "C" {
 #define SKSSM_COEF_FIXED 0 /* bufs->C: one fp32 map per head, shared by all sequences */
 #define SKSSM_COEF_STATE 1 /* bufs->Cstate: one map per (sequence, head), written by the flush */
 
+/* evaluation of the effective query and the buffered term at a non-flush
+ * read (GDN and KDA; a Mamba-2 effective query is a decay only, and Mamba-2
+ * ignores the choice) */
+#define SKSSM_PULLBACK_SERIAL 0 /* one buffered transition at a time, newest first */
+#define SKSSM_PULLBACK_WY 1     /* every buffered slot's coefficient from one triangular
+                                   system over the slots (paper App. C.1), then q~ and
+                                   the buffered term as sums over the slots */
+
 /* flush flags */
 #define SKSSM_FLUSH_DUE 0 /* flush tiles whose ring holds W entries */
 #define SKSSM_FLUSH_ALL 1 /* flush every tile (prime U, or retire sequences) */
@@ -112,6 +120,7 @@ typedef struct {
   float coef_ridge;          /* SKSSM_COEF_STATE: ridge relative to the mean eigenvalue of
                                 the sketch's Gram matrix, lambda = coef_ridge * trace(G) / r_h;
                                 finite and > 0 (ignored for SKSSM_COEF_FIXED) */
+  int32_t pullback;          /* SKSSM_PULLBACK_SERIAL or SKSSM_PULLBACK_WY (non-flush reads) */
 } sketchssm_layer;
 
 typedef struct {

@@ -19,6 +19,7 @@ SKSSM_MAMBA2, SKSSM_GDN, SKSSM_KDA = 0, 1, 2
 SKSSM_F32, SKSSM_BF16 = 0, 1
 SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL = 0, 1
 SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
+SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY = 0, 1
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5
 SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP = 1, 2
 
@@ -31,7 +32,7 @@ class sketchssm_layer(C.Structure):
                 ("qk_groups", C.c_int32), ("dk", C.c_int32), ("dv", C.c_int32),
                 ("window", C.c_int32), ("act_dtype", C.c_int32), ("sketch_dtype", C.c_int32),
                 ("rank_offsets_host", C.POINTER(C.c_int32)), ("coef_map", C.c_int32),
-                ("coef_ridge", C.c_float)]
+                ("coef_ridge", C.c_float), ("pullback", C.c_int32)]
 
 
 class sketchssm_buffers(C.Structure):

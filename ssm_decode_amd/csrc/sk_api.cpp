@@ -66,6 +66,7 @@ int check_layer(const sketchssm_layer* L) {
   }
   if (!shape_supported(L->dk, L->dv)) return SKSSM_EDIM;
   if (L->coef_map != SKSSM_COEF_FIXED && L->coef_map != SKSSM_COEF_STATE) return SKSSM_EFLAG;
+  if (L->pullback != SKSSM_PULLBACK_SERIAL && L->pullback != SKSSM_PULLBACK_WY) return SKSSM_EFLAG;
   if (L->coef_map == SKSSM_COEF_STATE && !(isfinite(L->coef_ridge) && L->coef_ridge > 0.f))
     return SKSSM_EINVAL;
   if (L->window < 1 || L->window > kMaxW) return SKSSM_EDIM;
@@ -144,6 +145,7 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
     if (L->rank_offsets_host[h + 1] == L->rank_offsets_host[h]) p.dense_list[nd++] = (int16_t)h;
   p.ndense = nd;
   p.ridge = L->coef_ridge;
+  p.pullback = L->pullback;
   if (S) {
     p.q = S->q;
     p.k = S->k;
@@ -243,6 +245,6 @@ int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer) {
   }
 }
 
-int sketchssm_version(void) { return 100; }
+int sketchssm_version(void) { return 101; }
 
 }  // extern "C"

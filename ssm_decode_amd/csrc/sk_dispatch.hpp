@@ -44,8 +44,12 @@ static void launch_read(const Params& p, hipStream_t st) {
       hipLaunchKernelGGL((m2_dense_read_kernel<DK, DV, AT, UT, WMAX>), dim3(p.B * p.ndense), dim3(64), 0,
                          st, p);
   } else {
-    hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF>), dim3(dn_read_blocks(p.B, p.H)),
-                       dim3(64 * DN_TPW), 0, st, p);
+    if (p.pullback)
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, true>), dim3(dn_read_blocks(p.B, p.H)),
+                         dim3(64 * DN_TPW), 0, st, p);
+    else
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, false>), dim3(dn_read_blocks(p.B, p.H)),
+                         dim3(64 * DN_TPW), 0, st, p);
     if (p.ndense > 0)
       hipLaunchKernelGGL((dn_dense_read_kernel<DK, DV, AT, UT>), dim3(p.B * p.ndense), dim3(DND_THREADS), 0,
                          st, p);

@@ -34,6 +34,7 @@ struct Params {
   int ndense;           // dense-fallback heads, in head order in dense_list; their state
   int16_t dense_list[DENSE_LIST_MAX];  // copies are Sc[b][position in the list]
   float ridge;          // relative ridge of the state-dependent map
+  int pullback;         // GDN/KDA read: 0 serial effective query, 1 the triangular-system form
   const void* q;
   const void* k;
   const void* v;

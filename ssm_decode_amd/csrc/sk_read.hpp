@@ -514,7 +514,7 @@ constexpr int DN_TPW = 4;            // tiles (waves) per workgroup
 
 __host__ __device__ inline int dn_read_blocks(int B, int H) { return (B + DN_TPW - 1) / DN_TPW * H; }
 
-template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF>
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF, bool WY>
 __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   constexpr int EK = DK >= 64 ? DK / 64 : 1;
   constexpr int EV = DV >= 64 ? DV / 64 : 1;
@@ -523,6 +523,9 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   constexpr int CCH = 16 * DK / 4;               // 16-byte chunks of 16 rows of C
   constexpr int CPT = (CCH + NT - 1) / NT;
   __shared__ __align__(16) float s_c[COEF ? 1 : 16 * DK];
+  // the triangular system of the parallel pull-back, per wave: L [WMAX][WMAX], then d [WMAX]
+  constexpr int WYS = WMAX * WMAX + WMAX;
+  __shared__ __align__(16) float s_wy[WY ? DN_TPW * WYS : 1];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int W = p.W;
@@ -658,17 +661,95 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
         r[e] = kl ? dec * (r[e] - bd * vget(kv, e)) : 0.f;
       }
     };
-    entry(kcur, vcur, gcur, bcur);
+    if constexpr (!WY) {
+      entry(kcur, vcur, gcur, bcur);
 #pragma unroll
-    for (int i = WMAX - 2; i >= 0; --i) {
-      if (i < n0) {
-        float gsc[KG];
-        if (FAM == FAM_GDN) gsc[0] = lane_value(al_l, i);
-        else
+      for (int i = WMAX - 2; i >= 0; --i) {
+        if (i < n0) {
+          float gsc[KG];
+          if (FAM == FAM_GDN) gsc[0] = lane_value(al_l, i);
+          else
 #pragma unroll
-          for (int e = 0; e < KG; ++e) gsc[e] = gs[i][e];
-        entry(ks[i], vs[i], gsc, lane_value(be_l, i));
+            for (int e = 0; e < KG; ++e) gsc[e] = gs[i][e];
+          entry(ks[i], vs[i], gsc, lane_value(be_l, i));
+        }
       }
+    } else {
+      // ------------------- parallel pull-back (triangular system)
+      // Slots 0..n0, oldest first: ring slot i < n0, the step's own entry at
+      // n0.  With D(j,l) the product of the decays of slots j+1..l, the
+      // serial form's coefficients d_j = k_j . r_j solve
+      //   d_j + sum_{l>j} beta_l <k_j, D(j,l) k_l> d_l = <k_j, D(j,n0) q>;
+      // every pair product is formed first (independent wave sums), the
+      // system is solved by back substitution, then
+      //   q~ = D(-1,n0) q - sum_l beta_l d_l D(-1,l) k_l,  o_buf = sum_l beta_l d_l v_l.
+      float* Lw = s_wy + wv * WYS;
+      float* dw = Lw + WMAX * WMAX;
+      auto key = [&](int i) -> VecN<AT, EK> { return i < n0 ? ks[i < WMAX - 1 ? i : 0] : kcur; };
+      auto beta_of = [&](int i) { return i < n0 ? lane_value(be_l, i < WMAX - 1 ? i : 0) : bcur; };
+      auto decay = [&](int i, float (&D)[EK]) {   // D <- D (.) (slot i's decay)
+        if constexpr (FAM == FAM_GDN) {
+          const float a = i < n0 ? lane_value(al_l, i < WMAX - 1 ? i : 0) : gcur[0];
+#pragma unroll
+          for (int e = 0; e < EK; ++e) D[e] *= a;
+        } else {
+#pragma unroll
+          for (int e = 0; e < EK; ++e) D[e] *= i < n0 ? gs[i < WMAX - 1 ? i : 0][e] : gcur[e];
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < WMAX; ++j) {
+        if (j <= n0) {                             // uniform
+          const VecN<AT, EK> kj = key(j);
+          float D[EK];
+#pragma unroll
+          for (int e = 0; e < EK; ++e) D[e] = 1.f;
+#pragma unroll
+          for (int l = j + 1; l < WMAX; ++l) {
+            if (l <= n0) {
+              decay(l, D);                         // D = D(j, l)
+              const VecN<AT, EK> kv = key(l);
+              float part = 0.f;
+#pragma unroll
+              for (int e = 0; e < EK; ++e) part += vget(kj, e) * D[e] * vget(kv, e);
+              const float Ljl = beta_of(l) * wave_sum(kl ? part : 0.f);   // (lanes without key elements hold copies)
+              if (lane == 0) Lw[j * WMAX + l] = Ljl;
+            }
+          }
+          float part = 0.f;                        // D = D(j, n0); r is q here (0 where !kl)
+#pragma unroll
+          for (int e = 0; e < EK; ++e) part += vget(kj, e) * D[e] * r[e];
+          const float bj = wave_sum(part);
+          if (lane == 0) dw[j] = bj;
+        }
+      }
+      // back substitution, wave-uniform (lane 0 keeps the solution in LDS;
+      // a wave's LDS accesses complete in order)
+#pragma unroll 1
+      for (int j = n0; j >= 0; --j) {
+        float t = dw[j];
+#pragma unroll 1
+        for (int l = j + 1; l <= n0; ++l) t -= Lw[j * WMAX + l] * dw[l];
+        if (lane == 0) dw[j] = t;
+      }
+      float D[EK], acc[EK];
+#pragma unroll
+      for (int e = 0; e < EK; ++e) { D[e] = 1.f; acc[e] = 0.f; }
+#pragma unroll
+      for (int l = 0; l < WMAX; ++l) {
+        if (l <= n0) {
+          decay(l, D);                             // D = D(-1, l)
+          const float bd = beta_of(l) * dw[l];
+          const VecN<AT, EK> kv = key(l);
+          const VecN<AT, EV> vv = l < n0 ? vs[l < WMAX - 1 ? l : 0] : vcur;
+#pragma unroll
+          for (int e = 0; e < EK; ++e) acc[e] -= bd * D[e] * vget(kv, e);
+#pragma unroll
+          for (int e = 0; e < EV; ++e) ob[e] += bd * vget(vv, e);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EK; ++e) r[e] = kl ? D[e] * r[e] + acc[e] : 0.f;
     }
 
     // -------------------------- c = C_h r, then o = U_h c + o_buf

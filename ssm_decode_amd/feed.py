@@ -26,10 +26,10 @@ def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def make_layer(cfg: synth.LayerConfig, li: synth.LayerInputs, device="cuda", coef: str = "fixed",
-               ridge: float = 1e-4) -> DecodeLayer:
+               ridge: float = 1e-4, pullback: str = "serial") -> DecodeLayer:
     lay = DecodeLayer(cfg.family, cfg.batch, cfg.heads, cfg.qk_groups, cfg.dk, cfg.dv,
                       cfg.window, cfg.act, cfg.sketch, li.offsets, device=device, coef=coef,
-                      ridge=ridge)
+                      ridge=ridge, pullback=pullback)
     lay.Pt.copy_(to_device(li.Pt, "f32", device))
     lay.Cmap.copy_(to_device(li.C, "f32", device))
     if li.A is not None:

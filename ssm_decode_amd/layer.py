@@ -41,6 +41,7 @@ class DeviceStep:
 
 
 COEF = {"fixed": abi.SKSSM_COEF_FIXED, "state": abi.SKSSM_COEF_STATE}
+PULLBACK = {"serial": abi.SKSSM_PULLBACK_SERIAL, "wy": abi.SKSSM_PULLBACK_WY}
 
 
 class DecodeLayer:
@@ -48,16 +49,20 @@ class DecodeLayer:
     ring (k, v, gate, beta), the per-tile ring counts, A, the error word and
     the read's workspace.  coef = "fixed" reads the per-head map Cmap;
     coef = "state" has every flush write each tile's own map into Cstate
-    ([B][R][dk], sketch dtype) with the relative ridge ``ridge``."""
+    ([B][R][dk], sketch dtype) with the relative ridge ``ridge``.
+    pullback = "serial" or "wy" selects how a GDN/KDA read evaluates the
+    effective query and the buffered term (Mamba-2 ignores it)."""
 
     def __init__(self, family: str, batch: int, heads: int, qk_groups: int, dk: int, dv: int,
                  window: int, act: str, sketch: str, rank_offsets: np.ndarray,
-                 device: str = "cuda", coef: str = "fixed", ridge: float = 1e-4):
+                 device: str = "cuda", coef: str = "fixed", ridge: float = 1e-4,
+                 pullback: str = "serial"):
         self.family, self.B, self.H, self.G = family, batch, heads, qk_groups
         self.dk, self.dv, self.W = dk, dv, window
         self.act, self.sketch = act, sketch
         self.device = device
         self.coef, self.ridge = coef, float(ridge)
+        self.pullback = pullback
         self.offsets_host = np.ascontiguousarray(np.asarray(rank_offsets, dtype=np.int32))
         self.R = int(self.offsets_host[-1])
         at, ut = TORCH_DTYPE[act], TORCH_DTYPE[sketch]
@@ -92,7 +97,7 @@ class DecodeLayer:
         self._layer = abi.sketchssm_layer(
             FAMILY[family], B, H, G, dk, dv, W, DTYPE[act], DTYPE[sketch],
             self.offsets_host.ctypes.data_as(C.POINTER(C.c_int32)), COEF[coef],
-            self.ridge if coef == "state" else 0.0)
+            self.ridge if coef == "state" else 0.0, PULLBACK[pullback])
         nwork = abi.sketchssm_workspace_bytes(self._layer)
         if nwork < 0:
             raise ValueError(f"invalid layer description (code {nwork})")

@@ -72,10 +72,12 @@ def all_tiles(cfg) -> np.ndarray:
 
 def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray = None,
                numpy_all: bool = True, li: synth.LayerInputs = None, log=True,
-               coef: str = "fixed", ridge: float = 1e-4) -> ParityReport:
+               coef: str = "fixed", ridge: float = 1e-4, pullback: str = "serial") -> ParityReport:
     """coef = "state": the flush forms each tile's own coefficient map with the
     relative ridge ``ridge`` (both sides use its fp32 value) and the maps of
-    the flushed tiles are compared too."""
+    the flushed tiles are compared too.  pullback = "wy": both sides evaluate
+    the effective query of a GDN/KDA read from the triangular system over
+    the buffered slots."""
     t0 = time.time()
     steps = cfg.steps if steps is None else steps
     li = synth.make_layer_inputs(cfg) if li is None else li
@@ -86,7 +88,7 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     W = cfg.window
 
     # --- HIP side
-    lay = feed.make_layer(cfg, li, coef=coef, ridge=ridge)
+    lay = feed.make_layer(cfg, li, coef=coef, ridge=ridge, pullback=pullback)
     feed.fill_state(lay, cfg, exact_seqs=seqs, numpy_all=numpy_all)
     # --- oracle side
     S0s = synth.initial_state(cfg, b_idx=seqs)
@@ -94,7 +96,7 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     orc = oracle.OracleLayer(cfg.family, cfg.dk, cfg.dv, W, li.ranks, li.offsets, li.Pt, li.C, li.A,
                              tiles, S0_t, cfg.heads, cfg.qk_groups, state_store="f32",
                              sketch_store=cfg.sketch, out_store=cfg.act, coef=coef,
-                             ridge=float(np.float32(ridge)))
+                             ridge=float(np.float32(ridge)), pullback=pullback)
     count0_t = li.count0[tiles[:, 0], tiles[:, 1]]
     if method == "sketch":
         assert feed.prime(lay, li) == 0
@@ -104,7 +106,8 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
         lay.count.copy_(torch.from_numpy(li.count0).to(lay.device))
     orc.count[:] = count0_t if method != "standard" else 0
 
-    rep = ParityReport(cfg.name, method + ("" if coef == "fixed" else "/state-map"), steps, len(tiles))
+    rep = ParityReport(cfg.name, method + ("" if coef == "fixed" else "/state-map")
+                       + ("" if pullback == "serial" else "/wy"), steps, len(tiles))
 
     def compare_maps(sel):
         C_gpu = lay.Cstate[tiles[sel, 0]].float().cpu().numpy().astype(np.float64)

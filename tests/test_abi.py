@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(abi.ENTRY_POINTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert abi.sketchssm_version() == 100
+    assert abi.sketchssm_version() == 101
 
 
 def test_header_constants_match_binding():
@@ -214,6 +214,19 @@ def test_coefficient_map_mode(lib):
     Lf = _layer(OK_OFF, batch=0)
     assert _all_calls(Lf, _bufs(Cstate=None), _step()) == [0] * 4
     assert abi.sketchssm_read(_layer(OK_OFF), _bufs(C=None), _step()) == abi.SKSSM_EINVAL
+
+
+def test_pullback_mode(lib):
+    """The pull-back mode is a flag: serial or the triangular-system form;
+    unknown values are EFLAG on every call."""
+    for bad in (2, -1):
+        L = _layer(OK_OFF, family=abi.SKSSM_GDN)
+        L.pullback = bad
+        assert _all_calls(L, _bufs(), _step()) == [abi.SKSSM_EFLAG] * 4
+    for fam in (abi.SKSSM_MAMBA2, abi.SKSSM_GDN, abi.SKSSM_KDA):
+        L = _layer(OK_OFF, family=fam, batch=0)
+        L.pullback = abi.SKSSM_PULLBACK_WY
+        assert _all_calls(L, _bufs(), _step()) == [0] * 4
 
 
 def test_dense_fallback_heads(lib):

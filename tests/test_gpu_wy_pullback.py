@@ -1,0 +1,73 @@
+"""The parallel (triangular-system) pull-back of the GDN/KDA read on the GPU
+against the oracle's own parallel form (needs a GPU).  Outputs, states and
+sketches at the usual tolerances, over several windows, in the layouts the
+serial form is tested in: small ragged layers, both window capacities,
+64x64 heads, tiny gates, the state-dependent map, dense-fallback heads and
+the full batch in the benchmark's launch configuration (sampled tiles)."""
+import pytest
+
+from synth import CONFIGS, LayerConfig
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ssm_decode_amd import abi
+    abi.load()
+
+
+def run(cfg, **kw):
+    from tests.gpu_parity import run_parity
+    print(f"\n[wy pull-back] {cfg.name} B={cfg.batch} H={cfg.heads} W={cfg.window} "
+          f"ragged={cfg.ragged} {kw.get('coef', 'fixed')}", flush=True)
+    return run_parity(cfg, "sketch", pullback="wy", **kw)
+
+
+def _tiny(family, seed, **kw):
+    base = dict(name=f"tiny_wy_{family}", family=family, batch=3, heads=4, qk_groups=4, dk=16,
+                dv=32, window=6, mean_rank=4, fixed_rank=4, act="f32", sketch="f32", steps=26,
+                ragged=True, seed=seed)
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+@pytest.mark.parametrize("family,seed", [("gdn", 61), ("kda", 62)])
+def test_tiny(family, seed):
+    run(_tiny(family, seed))
+
+
+@pytest.mark.parametrize("family,W", [("gdn", 1), ("kda", 2), ("gdn", 16), ("kda", 32)])
+def test_window_sizes(family, W):
+    run(_tiny(family, 63 + W, window=W, steps=2 * W + 5, name=f"tiny_wy_{family}_W{W}"))
+
+
+@pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
+def test_small_batch_ragged(name):
+    run(CONFIGS[name].with_(name=name + "_wy", batch=3, ragged=True, steps=36))
+
+
+@pytest.mark.parametrize("family", ["gdn", "kda"])
+def test_head_64x64(family):
+    run(CONFIGS[family + "_b256"].with_(name=f"{family}_64x64_wy", dk=64, dv=64, batch=2, steps=20,
+                                         ragged=True))
+
+
+def test_state_map_and_dense_heads():
+    run(CONFIGS["kda_b256"].with_(name="kda_wy_map_dense", batch=2, ragged=True, steps=24,
+                                  dense_heads=(3,)), coef="state")
+    run(CONFIGS["gdn_b256"].with_(name="gdn_wy_dense", batch=2, ragged=True, steps=24,
+                                  dense_heads=(0, 7)))
+
+
+@pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
+def test_full_batch_sampled(name):
+    """Full batch in the benchmark's launch configuration, the oracle
+    following sampled tiles."""
+    from tests.gpu_parity import sample_tiles
+    cfg = CONFIGS[name]
+    run(cfg, steps=2 * cfg.window + 6, tiles=sample_tiles(cfg, 3, 3, seed=cfg.seed), numpy_all=False)
