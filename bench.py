@@ -414,12 +414,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891451676,
-                "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
-    "gdn_b256": {"bytes": 1155965569,
-                 "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
-    "kda_b256": {"bytes": 1213752728,
-                 "src_sha256": "2c1386775ffb51ec7234aa0a056b5a250e3d68e0fee266f9abc625b990a24adb"},
+    "m2_b320": {"bytes": 2891449364,
+                "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
+    "gdn_b256": {"bytes": 1155965936,
+                 "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
+    "kda_b256": {"bytes": 1213770406,
+                 "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
