@@ -179,7 +179,8 @@ __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
       rp = p.C + (size_t)(roff0 + rr) * DK;
     }
 #pragma unroll
-    for (int k = 0; k < NCL; ++k) c[bb][k] = ldraw<CE>(rp + CE * (qt + CQ_LPR * k));
+    for (int k = 0; k < NCL; ++k)   // (a sequence's own map rows are read once: non-temporal)
+      c[bb][k] = COEF ? ldraw_nt<CE>(rp + CE * (qt + CQ_LPR * k)) : ldraw<CE>(rp + CE * (qt + CQ_LPR * k));
   }
   const AT* q = reinterpret_cast<const AT*>(p.q);
   float qv[QIT][4];
@@ -612,7 +613,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
     const UT* Csb = reinterpret_cast<const UT*>(p.Cs) + ((size_t)bcl * p.R + off) * DK + lk;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < rk && rd) ldn<EK>(Csb + (size_t)j * DK, cr[j]);
+      if (j < rk && rd) ldn<EK>(Csb + (size_t)j * DK, cr[j]);   // (non-temporal measured slower here)
   }
   VecN<UT, EV> us[16];
   const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)bcl * p.R + off) * DV + lv;
