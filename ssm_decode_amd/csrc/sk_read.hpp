@@ -724,14 +724,19 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
           if (lane == 0) dw[j] = bj;
         }
       }
-      // back substitution, wave-uniform (lane 0 keeps the solution in LDS;
-      // a wave's LDS accesses complete in order)
-#pragma unroll 1
-      for (int j = n0; j >= 0; --j) {
-        float t = dw[j];
-#pragma unroll 1
-        for (int l = j + 1; l <= n0; ++l) t -= Lw[j * WMAX + l] * dw[l];
-        if (lane == 0) dw[j] = t;
+      // back substitution: lane l holds d_l once it is known and reads row j
+      // of the table at column l, so each d_j is one wave sum (the table
+      // reads do not wait for the solution; a wave's LDS accesses complete
+      // in order, so lane 0's writes above are visible)
+      float dlane = 0.f;
+#pragma unroll
+      for (int j = WMAX - 1; j >= 0; --j) {
+        if (j <= n0) {                             // uniform
+          const int lc = lane < WMAX ? lane : 0;
+          const float Ljl = (lane > j && lane <= n0) ? Lw[j * WMAX + lc] : 0.f;
+          const float dj = dw[j] - wave_sum(Ljl * dlane);
+          dlane = lane == j ? dj : dlane;
+        }
       }
       float D[EK], acc[EK];
 #pragma unroll
@@ -740,7 +745,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
       for (int l = 0; l < WMAX; ++l) {
         if (l <= n0) {
           decay(l, D);                             // D = D(-1, l)
-          const float bd = beta_of(l) * dw[l];
+          const float bd = beta_of(l) * lane_value(dlane, l);
           const VecN<AT, EK> kv = key(l);
           const VecN<AT, EV> vv = l < n0 ? vs[l < WMAX - 1 ? l : 0] : vcur;
 #pragma unroll
