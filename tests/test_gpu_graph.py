@@ -1,0 +1,83 @@
+"""The benchmark times decode steps captured in a HIP graph (needs a GPU).
+A captured sequence of reads and flushes, replayed, must give bit-identical
+outputs, states, sketches, maps, state copies, rings, counts and error word
+to the same calls made eagerly, on every replay, with the program's own
+eager work (restoring the buffers) between the replays."""
+import pytest
+
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ssm_decode_amd import abi
+    abi.load()
+
+
+def _buffers(lay):
+    names = ("S", "U", "Cstate", "Scopy", "ring_k", "ring_v", "ring_gate", "ring_beta", "count", "err")
+    return {n: getattr(lay, n) for n in names if getattr(lay, n) is not None}
+
+
+CASES = [
+    ("tiny_m2", {}, "fixed", "serial"),
+    ("m2_b320", dict(batch=3, ragged=True, dense_heads=(5, 70)), "fixed", "serial"),
+    ("gdn_b256", dict(batch=3, ragged=True), "fixed", "serial"),
+    ("gdn_b256", dict(batch=2, ragged=True, dense_heads=(1,)), "fixed", "wy"),
+    ("kda_b256", dict(batch=2, ragged=True), "state", "serial"),
+]
+
+
+@pytest.mark.parametrize("name,over,coef,pullback", CASES)
+def test_graph_replay_matches_eager(name, over, coef, pullback):
+    import synth
+    from ssm_decode_amd import abi, feed
+    cfg = CONFIGS[name].with_(name=name + "_graph", **over)
+    print(f"\n[graph] {cfg.name} B={cfg.batch} W={cfg.window} {coef} {pullback}", flush=True)
+    li = synth.make_layer_inputs(cfg)
+    lay = feed.make_layer(cfg, li, coef=coef, pullback=pullback)
+    feed.fill_state(lay, cfg)
+    assert feed.prime(lay, li) == 0
+    K = 2 * cfg.window + 3
+    steps = [lay.new_step() for _ in range(K)]
+    for t, st in enumerate(steps):
+        feed.fill_step(st, cfg, t)
+    torch.cuda.synchronize()
+    start = {n: b.clone() for n, b in _buffers(lay).items()}
+
+    def restore():
+        for n, b in _buffers(lay).items():
+            b.copy_(start[n])
+        for st in steps:
+            st.o.zero_()
+
+    def run(stream):
+        for st in steps:
+            assert lay.read(st, stream=stream) == 0
+            assert lay.flush(st, abi.SKSSM_FLUSH_DUE, stream=stream) == 0
+
+    run(None)                                  # eager
+    torch.cuda.synchronize()
+    eager_o = [st.o.clone() for st in steps]
+    eager_b = {n: b.clone() for n, b in _buffers(lay).items()}
+
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, st in enumerate(steps):
+            assert torch.equal(st.o, eager_o[t]), (rep, "o", t)
+        for n, b in _buffers(lay).items():
+            assert torch.equal(b, eager_b[n]), (rep, n)
