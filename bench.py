@@ -414,12 +414,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891449364,
-                "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
-    "gdn_b256": {"bytes": 1155965936,
-                 "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
-    "kda_b256": {"bytes": 1213770406,
-                 "src_sha256": "b23783045a993c8d7fa9c3e052fb8cd69bced3c888a87954f968e7f596cad21f"},
+    "m2_b320": {"bytes": 2891443583,
+                "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
+    "gdn_b256": {"bytes": 1155952760,
+                 "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
+    "kda_b256": {"bytes": 1213790034,
+                 "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
