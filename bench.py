@@ -414,12 +414,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891438650,
-                "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
-    "gdn_b256": {"bytes": 1155943101,
-                 "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
-    "kda_b256": {"bytes": 1213774463,
-                 "src_sha256": "70bb719547025784029328ad73ef9bd21d24a4c64a4b91150368ed138fdafd87"},
+    "m2_b320": {"bytes": 2891453069,
+                "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
+    "gdn_b256": {"bytes": 1155956362,
+                 "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
+    "kda_b256": {"bytes": 1213765303,
+                 "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 

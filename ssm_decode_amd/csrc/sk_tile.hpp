@@ -127,6 +127,40 @@ __device__ __forceinline__ f32x4v mfma16x4(float a, float b, f32x4v d) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, d, 0, 0, 0);
 }
 
+// Row R of 16 lanes broadcast to all four rows (two lane-swap steps).
+template <int R>
+__device__ __forceinline__ float row_bcast(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const unsigned a = (R & 1) ? s[1] : s[0];
+  const auto t = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  return __uint_as_float((R & 2) ? t[1] : t[0]);
+}
+
+// One pivot of the in-place Gauss-Jordan inversion of a 16 x 16 matrix held
+// as lane (cg, rg): m[v] = M[4 rg + v][cg].
+template <int K>
+__device__ __forceinline__ void gj_pivot(float (&m)[4], int cg, int rg) {
+  const float mkj = row_bcast<K / 4>(m[K & 3]);                 // M[K][cg]
+  float mik[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)                                   // M[4 rg + v][K]: row_newbcast:K
+    mik[v] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m[v]), 0x150 + K, 0xF, 0xF, false));
+  const float piv = 1.f / __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mkj), K));
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i = 4 * rg + v;
+    if (i == K) m[v] = (cg == K) ? piv : mkj * piv;
+    else m[v] = (cg == K) ? -mik[v] * piv : m[v] - mik[v] * (mkj * piv);
+  }
+}
+template <int K>
+__device__ __forceinline__ void gj_invert(float (&m)[4], int cg, int rg) {
+  if constexpr (K < 16) {
+    gj_pivot<K>(m, cg, rg);
+    gj_invert<K + 1>(m, cg, rg);
+  }
+}
+
 // State-dependent coefficient map of one tile at the flush (project page,
 // per-window flush panel: C = (U^T U)^+ U^T S0^T; paper App. A.2.1-A.2.2):
 // with U_h the sketch rows as stored (rounded to the sketch dtype) and S the
@@ -229,20 +263,7 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
     // in-place Gauss-Jordan inversion, pivot k: with p = 1 / M[k][k],
     //   M[k][k] <- p,            M[k][j] <- M[k][j] p              (j != k)
     //   M[i][k] <- -M[i][k] p,   M[i][j] <- M[i][j] - M[i][k] M[k][j] p
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float mkj = __shfl(m[k & 3], (k >> 2) * 16 + cg);     // M[k][cg]
-      float mik[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mik[v] = __shfl(m[v], rg * 16 + k);   // M[4 rg + v][k]
-      const float piv = 1.f / lane_value(mkj, k);                // lane k holds M[k][k]
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = 4 * rg + v;
-        if (i == k) m[v] = (cg == k) ? piv : mkj * piv;
-        else m[v] = (cg == k) ? -mik[v] * piv : m[v] - mik[v] * (mkj * piv);
-      }
-    }
+    gj_invert<0>(m, cg, rg);
     // inverse row-major: s_gi[i][j]
 #pragma unroll
     for (int v = 0; v < 4; ++v) s_gi[(4 * rg + v) * 16 + cg] = m[v];
@@ -263,6 +284,8 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
   const float4 ga4 = *reinterpret_cast<const float4*>(s_gi + cg * 16 + 4 * rg);
   const float ga[4] = {ga4.x, ga4.y, ga4.z, ga4.w};
   UT* Cb = reinterpret_cast<UT*>(p.Cs) + ((size_t)b * p.R + off) * DK;
+  constexpr bool STAGE = sizeof(UT) == 2 && 16 * DK * 2 <= LY::PART * 4;
+  UT* s_cm = reinterpret_cast<UT*>(smem + LY::SST);   // [16][DK] (STAGE)
 #pragma unroll
   for (int q = 0; q < MBW; ++q) {
     const int mb = wv + q * NCB;
@@ -274,8 +297,18 @@ __device__ __forceinline__ void coef_map(const Params& p, float* smem,
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 4 * rg + v;
-        if (j < r) st(Cb + (size_t)j * DK + 16 * mb + cg, cm[v]);
+        if constexpr (STAGE) s_cm[j * DK + 16 * mb + cg] = Store<UT>::cvt(cm[v]);
+        else if (j < r) st(Cb + (size_t)j * DK + 16 * mb + cg, cm[v]);
       }
+    }
+  }
+  if constexpr (STAGE) {
+    // whole rows, 16 bytes a thread
+    constexpr int CPR = DK * 2 / 16;                 // 16-byte chunks per row
+    __syncthreads();
+    for (int c = threadIdx.x; c < r * CPR; c += (int)blockDim.x) {
+      const int j = c / CPR, ch = c - j * CPR;
+      reinterpret_cast<uint4*>(Cb + (size_t)j * DK)[ch] = reinterpret_cast<const uint4*>(s_cm + j * DK)[ch];
     }
   }
 }
