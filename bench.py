@@ -44,6 +44,8 @@ def parse():
                     help="skip the run with the state-dependent coefficient map")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the run with dense-fallback heads")
+    ap.add_argument("--flush-list", action="store_true",
+                    help="ragged phase: flush through sketchssm_flush_seqs with each step's due sequences")
     ap.add_argument("--no-wy", action="store_true",
                     help="skip the GDN/KDA run with the triangular-system pull-back")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
@@ -127,6 +129,14 @@ def main():
     phase = int(li.phase[0])
     ragged = cfg.ragged
     K = args.steps
+    # listed flush: the sequences whose window closes at step t (t mod W),
+    # from each sequence's initial ring fill; device-resident for the graph
+    flush_lists = None
+    if args.flush_list and ragged:
+        c0 = np.asarray(li.count0)
+        assert (c0 == c0[:, :1]).all(), "one window phase per sequence"
+        flush_lists = [torch.from_numpy(np.nonzero((c0[:, 0] + r + 1) % W == 0)[0].astype(np.int32)).to(dev)
+                       for r in range(W)]
 
     def measure(layers):
         """Event-timed eager kernels over two windows, then exactly K steps
@@ -148,8 +158,14 @@ def main():
                     if ev is not None:
                         ev["flush"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
                         ev["flush"][-1][0].record(stream)
-                    rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
-                                             abi.SKSSM_FLUSH_DUE, sh_)
+                    if flush_lists is not None:
+                        dl = flush_lists[t % W]
+                        rc = abi.sketchssm_flush_seqs(lay.layer_struct, lay.buffers_struct, st,
+                                                      ctypes.c_void_p(dl.data_ptr()) if dl.numel() else None,
+                                                      int(dl.numel()), sh_)
+                    else:
+                        rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
+                                                 abi.SKSSM_FLUSH_DUE, sh_)
                     if ev is not None:
                         ev["flush"][-1][1].record(stream)
                     assert rc == 0
@@ -375,6 +391,7 @@ def main():
             "qk_groups": cfg.qk_groups, "dk": cfg.dk, "dv": cfg.dv, "window": W,
             "mean_rank": cfg.mean_rank, "state": "f32", "act": cfg.act, "sketch": cfg.sketch,
             "layers_rotated": L, "windows_exact": windows_exact,
+            "flush": "listed sequences (sketchssm_flush_seqs)" if flush_lists is not None else "due flag",
         },
         "achieved_gbs": round(achieved_gbs, 1),
         "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),

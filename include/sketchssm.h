@@ -98,6 +98,7 @@ extern "C" {
 /* bits OR-ed into *err by the kernels */
 #define SKSSM_ERRBIT_COUNT 1  /* count outside [0, W] (or == W at a read) */
 #define SKSSM_ERRBIT_GROUP 2  /* Mamba-2 heads of one B/C group disagree on count */
+#define SKSSM_ERRBIT_SEQ 4    /* sketchssm_flush_seqs: a listed index outside [0, batch) */
 
 /* Supported shapes: (dk, dv) in {(16,32), (64,64), (128,64), (128,128)};
  * 1 <= W <= 32; 0 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16
@@ -191,6 +192,21 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,
                     void* hip_stream);
+
+/* Flush of listed sequences: sketchssm_flush with SKSSM_FLUSH_DUE, launched
+ * for the tiles of the nseq sequences in seqs only (paper App. B: each
+ * sequence flushes when its own window fills).  For callers that know which
+ * sequences close their window at this step: under a ragged window phase
+ * about batch / W sequences are due per step, and the due-flag flush pays
+ * for a workgroup per tile of the whole batch.  seqs: DEVICE array of nseq
+ * distinct sequence indices (int32, 4-byte aligned), 0 <= nseq <= batch.
+ * A listed tile whose count is not W is left alone; an index outside
+ * [0, batch) sets SKSSM_ERRBIT_SEQ and is skipped.  Two equal indices in one
+ * list would flush the same tiles at once: the caller keeps them distinct.
+ * nseq = 0 launches nothing. */
+int sketchssm_flush_seqs(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                         const sketchssm_step* step /* NULL: no output */, const int32_t* seqs,
+                         int32_t nseq, void* hip_stream);
 
 /* Standard full-state step (project page "01 / The idea": S_t = M_t S_{t-1}
  * + B_t, o_t = S_t^T q_t): S <- M S + B and o = S^T q for every tile.

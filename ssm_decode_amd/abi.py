@@ -21,9 +21,9 @@ SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL = 0, 1
 SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
 SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY = 0, 1
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5
-SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP = 1, 2
+SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP, SKSSM_ERRBIT_SEQ = 1, 2, 4
 
-ENTRY_POINTS = ("sketchssm_read", "sketchssm_flush", "sketchssm_full_step",
+ENTRY_POINTS = ("sketchssm_read", "sketchssm_flush", "sketchssm_flush_seqs", "sketchssm_full_step",
                 "sketchssm_replay_step", "sketchssm_workspace_bytes", "sketchssm_version")
 
 
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
             fn.restype = C.c_int
         lib.sketchssm_flush.argtypes = [L, Bf, St, C.c_int32, C.c_void_p]
         lib.sketchssm_flush.restype = C.c_int
+        lib.sketchssm_flush_seqs.argtypes = [L, Bf, St, C.c_void_p, C.c_int32, C.c_void_p]
+        lib.sketchssm_flush_seqs.restype = C.c_int
         lib.sketchssm_workspace_bytes.argtypes = [L]
         lib.sketchssm_workspace_bytes.restype = C.c_int64
         lib.sketchssm_version.argtypes = []
@@ -90,6 +92,12 @@ def sketchssm_read(layer, bufs, step, stream=None) -> int:
 def sketchssm_flush(layer, bufs, step, flags, stream=None) -> int:
     return load().sketchssm_flush(_ref(layer, sketchssm_layer), _ref(bufs, sketchssm_buffers),
                                   _ref(step, sketchssm_step), int(flags), stream)
+
+
+def sketchssm_flush_seqs(layer, bufs, step, seqs, nseq, stream=None) -> int:
+    """seqs: device address of nseq int32 sequence indices (or None with nseq = 0)."""
+    return load().sketchssm_flush_seqs(_ref(layer, sketchssm_layer), _ref(bufs, sketchssm_buffers),
+                                       _ref(step, sketchssm_step), seqs, int(nseq), stream)
 
 
 def sketchssm_full_step(layer, bufs, step, stream=None) -> int:

@@ -209,6 +209,30 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
   }
 }
 
+int sketchssm_flush_seqs(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                         const sketchssm_step* step, const int32_t* seqs, int32_t nseq, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    if (nseq < 0 || nseq > layer->batch) return SKSSM_EDIM;
+    if (nseq > 0 && (!seqs || (reinterpret_cast<uintptr_t>(seqs) & 3))) return SKSSM_EINVAL;
+    const bool out = step != nullptr;
+    const Needs nd{true, true, true, false, true, true, false, out, out, false, true};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    if (nseq == 0) return SKSSM_OK;
+    sk::Params p = make_params(layer, bufs, step);
+    p.seq_list = seqs;
+    p.nseq = nseq;
+    if (!out) {
+      p.q = nullptr;
+      p.o = nullptr;
+    }
+    return dispatch(layer, sk::MODE_FLUSH, p, hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
 int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                         const sketchssm_step* step, void* hip_stream) {
   try {
@@ -245,6 +269,6 @@ int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer) {
   }
 }
 
-int sketchssm_version(void) { return 101; }
+int sketchssm_version(void) { return 102; }
 
 }  // extern "C"

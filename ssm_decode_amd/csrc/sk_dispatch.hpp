@@ -9,7 +9,7 @@ namespace sk {
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
 static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
-  const dim3 grid(p.B * p.H), block(TileShape<DK, DV>::THREADS);
+  const dim3 grid((p.seq_list ? p.nseq : p.B) * p.H), block(TileShape<DK, DV>::THREADS);
   constexpr size_t lds_flush = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH, 0>::BYTES;
   constexpr size_t lds_flush_map = TileLds<FAM, DK, DV, WMAX, MODE_FLUSH, 1>::BYTES;
   constexpr size_t lds_full = TileLds<FAM, DK, DV, WMAX, MODE_FULL, 0>::BYTES;

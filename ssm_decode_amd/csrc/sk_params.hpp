@@ -9,13 +9,15 @@ namespace sk {
 enum Family { FAM_M2 = 0, FAM_GDN = 1, FAM_KDA = 2 };
 enum Mode { MODE_FLUSH = 0, MODE_FULL = 1, MODE_REPLAY = 2, MODE_READ = 3 };
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
-enum ErrBit { ERRBIT_COUNT = 1, ERRBIT_GROUP = 2 };
+enum ErrBit { ERRBIT_COUNT = 1, ERRBIT_GROUP = 2, ERRBIT_SEQ = 4 };
 
 constexpr int DENSE_LIST_MAX = 64;   // dense-fallback heads listed in the kernel arguments
 
 struct Params {
   int B, H, G, HPG, W, R;
   int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
+  const int32_t* seq_list;  // MODE_FLUSH: device list of nseq sequences to flush, or null (all)
+  int nseq;
   float* S;
   void* U;
   const float* Pt;

@@ -342,8 +342,16 @@ tile_kernel(Params p) {
   const int cg = lane & 15;
   const int rg = lane >> 4;
   const int tile = blockIdx.x;
-  const int b = tile / p.H;
-  const int h = tile - b * p.H;
+  const int ts = tile / p.H;
+  const int h = tile - ts * p.H;
+  int b = ts;
+  if (MODE == MODE_FLUSH && p.seq_list) {        // uniform: the tiles of listed sequences
+    b = p.seq_list[ts];
+    if (b < 0 || b >= p.B) {
+      if (threadIdx.x == 0) atomicOr(p.err, ERRBIT_SEQ);
+      return;
+    }
+  }
   const int g = h / p.HPG;
   const size_t bh = (size_t)b * p.H + h;
   const int colbase = wv * CB + NCC * cg;        // first of the lane's columns

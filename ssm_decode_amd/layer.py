@@ -142,6 +142,14 @@ class DecodeLayer:
         st = None if step is None else step.struct()
         return abi.sketchssm_flush(self._layer, self._bufs, st, flags, self._stream(stream))
 
+    def flush_seqs(self, step: Optional[DeviceStep], seqs, stream=None) -> int:
+        """Due-only flush of the sequences in seqs (an int32 device tensor of
+        distinct indices)."""
+        st = None if step is None else step.struct()
+        n = int(seqs.numel())
+        ptr = C.c_void_p(seqs.data_ptr()) if n else None
+        return abi.sketchssm_flush_seqs(self._layer, self._bufs, st, ptr, n, self._stream(stream))
+
     def full_step(self, step: DeviceStep, stream=None) -> int:
         return abi.sketchssm_full_step(self._layer, self._bufs, step.struct(), self._stream(stream))
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(abi.ENTRY_POINTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert abi.sketchssm_version() == 101
+    assert abi.sketchssm_version() == 102
 
 
 def test_header_constants_match_binding():
@@ -252,3 +252,19 @@ def test_dense_fallback_heads(lib):
                               _bufs(), _step()) == 0
     # with sketched heads the sketch is still required
     assert abi.sketchssm_read(_layer([0, 4, 4, 8, 12]), _bufs(U=None), _step()) == abi.SKSSM_EINVAL
+
+
+def test_flush_seqs_arguments():
+    """The listed flush checks its list on the host: count in [0, batch], a
+    4-byte aligned device pointer when the list is not empty; an empty list
+    launches nothing."""
+    import ctypes as C
+    L = _layer(OK_OFF, batch=2)
+    B = _bufs()
+    seqs = C.c_void_p(FAKE)
+    assert abi.sketchssm_flush_seqs(L, B, None, seqs, -1) == abi.SKSSM_EDIM
+    assert abi.sketchssm_flush_seqs(L, B, None, seqs, 3) == abi.SKSSM_EDIM
+    assert abi.sketchssm_flush_seqs(L, B, None, None, 1) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_flush_seqs(L, B, None, C.c_void_p(FAKE + 2), 1) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_flush_seqs(L, B, None, None, 0) == abi.SKSSM_OK
+    assert abi.sketchssm_flush_seqs(L, _bufs(S=FAKE + 4), None, seqs, 1) == abi.SKSSM_EINVAL
