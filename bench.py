@@ -431,12 +431,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891453069,
-                "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
-    "gdn_b256": {"bytes": 1155956362,
-                 "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
-    "kda_b256": {"bytes": 1213765303,
-                 "src_sha256": "53de93f6302e7492c5436a14870c7fc713097d8bbab4fd843f45e5a4f24ff636"},
+    "m2_b320": {"bytes": 2891453945,
+                "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
+    "gdn_b256": {"bytes": 1155957922,
+                 "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
+    "kda_b256": {"bytes": 1213532798,
+                 "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
