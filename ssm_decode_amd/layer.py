@@ -146,7 +146,11 @@ class DecodeLayer:
         """Due-only flush of the sequences in seqs (an int32 device tensor of
         distinct indices)."""
         st = None if step is None else step.struct()
+        if seqs.dtype != torch.int32 or seqs.dim() != 1 or not seqs.is_contiguous():
+            raise ValueError("seqs: a contiguous 1-d int32 tensor")
         n = int(seqs.numel())
+        if n and seqs.device.type != "cuda":
+            raise ValueError("seqs must be device memory")
         ptr = C.c_void_p(seqs.data_ptr()) if n else None
         return abi.sketchssm_flush_seqs(self._layer, self._bufs, st, ptr, n, self._stream(stream))
 

@@ -268,3 +268,20 @@ def test_flush_seqs_arguments():
     assert abi.sketchssm_flush_seqs(L, B, None, C.c_void_p(FAKE + 2), 1) == abi.SKSSM_EINVAL
     assert abi.sketchssm_flush_seqs(L, B, None, None, 0) == abi.SKSSM_OK
     assert abi.sketchssm_flush_seqs(L, _bufs(S=FAKE + 4), None, seqs, 1) == abi.SKSSM_EINVAL
+
+
+def test_flush_seqs_binding_rejects_host_or_wrong_lists():
+    """The Python binding refuses a list the kernel could not read: host
+    memory, another dtype, or a non-contiguous view (checked before any
+    call into the library)."""
+    import torch
+    from ssm_decode_amd.layer import DecodeLayer
+
+    class _Stub:                    # only the argument checks of flush_seqs run
+        flush_seqs = DecodeLayer.flush_seqs
+    with pytest.raises(ValueError):
+        _Stub().flush_seqs(None, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        _Stub().flush_seqs(None, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        _Stub().flush_seqs(None, torch.zeros(4, dtype=torch.int32)[::2])
