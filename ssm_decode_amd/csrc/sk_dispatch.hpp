@@ -36,7 +36,7 @@ static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF>
 static void launch_read(const Params& p, hipStream_t st) {
   if constexpr (FAM == FAM_M2) {
-    const dim3 pgrid(PrepGrid<COEF, DK, UT>::blocks(p.B), p.G);
+    const dim3 pgrid(PrepGrid<COEF, DK, UT, WMAX>::blocks(p.B), p.G);
     const dim3 rgrid(m2_read_blocks(p.B, p.G, p.HPG));
     hipLaunchKernelGGL((m2_prep_kernel<DK, AT, UT, WMAX, COEF>), pgrid, dim3(CQ_THREADS), 0, st, p);
     hipLaunchKernelGGL((m2_read_kernel<DK, DV, AT, UT, WMAX>), rgrid, dim3(64 * M2R_WPB), 0, st, p);

@@ -30,7 +30,11 @@ namespace sk {
 //   q~ = D q, D = prod_i a_i;   o_buf = sum_i w_i d_i v_i, w_i = dt_i prod_{t>i} a_t
 //   o  = D * U_h cq_h + o_buf
 constexpr int M2R_MAXHPG = 16;     // heads per B/C group (at most)
-constexpr int CQ_NB = 8;           // sequences per dot-product workgroup
+// Sequences per dot-product workgroup: 8, or 4 for a 32-slot ring, so that
+// the keys and queries in flight stay at two passes of registers (four
+// passes at W = 32 held the whole prep kernel to three waves per SIMD).
+template <int WMAX>
+constexpr int cq_nb() { return WMAX > 16 ? 4 : 8; }
 constexpr int CQ_THREADS = 256;
 // The prep grid is (dot-product blocks, then coefficient blocks) x groups.
 // A coefficient block takes ROWS coefficient rows of a group for NBC
@@ -39,8 +43,9 @@ constexpr int CQ_THREADS = 256;
 // sequence, read once (8 lanes a row at dk >= 64).  Larger blocks cut the L2
 // traffic of a fixed C but lengthen each workgroup's serial loop over its
 // sequences, which costs more.
-template <int COEF, int DK, typename UT>
+template <int COEF, int DK, typename UT, int WMAX = 16>
 struct PrepGrid {
+  static constexpr int CQ_NB = cq_nb<WMAX>();
   static constexpr int CSIZE = COEF ? (int)sizeof(UT) : 4;  // bytes per C element
   static constexpr int NCH = DK * CSIZE / 16;               // 16-byte chunks per C row
   static constexpr int LPR0 = COEF && DK >= 64 ? 8 : 4;
@@ -56,6 +61,7 @@ constexpr int DOT_LPP = 4;         // lanes per (sequence, slot) dot product
 
 template <int DK, typename AT, int WMAX>
 __device__ __forceinline__ void m2_prep_dots(const Params& p, int xb) {
+  constexpr int CQ_NB = cq_nb<WMAX>();
   // a key or query row is split into NCK chunks of CEK elements (16 bytes, or
   // a quarter row when that is smaller); lane qt of a pair takes chunks
   // qt, qt + 4, .. so that one load instruction reads whole 64-byte pieces
@@ -134,7 +140,7 @@ __device__ __forceinline__ void m2_prep_dots(const Params& p, int xb) {
 
 template <int DK, typename AT, typename UT, int WMAX, int COEF>
 __global__ void __launch_bounds__(CQ_THREADS) m2_prep_kernel(Params p) {
-  using PG = PrepGrid<COEF, DK, UT>;
+  using PG = PrepGrid<COEF, DK, UT, WMAX>;
   constexpr int CQ_LPR = PG::LPR, CQ_ROWS = PG::ROWS, NBC = PG::NBC;
   const int ndot = PG::dot_blocks(p.B);
   if ((int)blockIdx.x < ndot) {                    // uniform: a dot-product block
