@@ -431,12 +431,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891453945,
-                "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
-    "gdn_b256": {"bytes": 1155957922,
-                 "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
-    "kda_b256": {"bytes": 1213532798,
-                 "src_sha256": "23b11a1f7704bf329be7c7a6772a6806bf0f44c97472070dc662fee0cc4be416"},
+    "m2_b320": {"bytes": 2891445509,
+                "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
+    "gdn_b256": {"bytes": 1155942854,
+                 "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
+    "kda_b256": {"bytes": 1213516995,
+                 "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
 
