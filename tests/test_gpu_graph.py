@@ -2,7 +2,10 @@
 A captured sequence of reads and flushes, replayed, must give bit-identical
 outputs, states, sketches, maps, state copies, rings, counts and error word
 to the same calls made eagerly, on every replay, with the program's own
-eager work (restoring the buffers) between the replays."""
+eager work (restoring the buffers) between the replays.  The flush is the
+due-flag flush, or the flush of listed sequences with each step's due
+sequences (device lists made before the capture; the eager listed run is
+also checked against the eager due-flag run)."""
 import pytest
 
 from synth import CONFIGS
@@ -26,20 +29,22 @@ def _buffers(lay):
 
 
 CASES = [
-    ("tiny_m2", {}, "fixed", "serial"),
-    ("m2_b320", dict(batch=3, ragged=True, dense_heads=(5, 70)), "fixed", "serial"),
-    ("gdn_b256", dict(batch=3, ragged=True), "fixed", "serial"),
-    ("gdn_b256", dict(batch=2, ragged=True, dense_heads=(1,)), "fixed", "wy"),
-    ("kda_b256", dict(batch=2, ragged=True), "state", "serial"),
+    ("tiny_m2", {}, "fixed", "serial", "due"),
+    ("m2_b320", dict(batch=3, ragged=True, dense_heads=(5, 70)), "fixed", "serial", "due"),
+    ("gdn_b256", dict(batch=3, ragged=True), "fixed", "serial", "due"),
+    ("gdn_b256", dict(batch=2, ragged=True, dense_heads=(1,)), "fixed", "wy", "due"),
+    ("kda_b256", dict(batch=2, ragged=True), "state", "serial", "due"),
+    ("m2_b320", dict(batch=5, ragged=True), "fixed", "serial", "list"),
+    ("kda_b256", dict(batch=3, ragged=True), "state", "serial", "list"),
 ]
 
 
-@pytest.mark.parametrize("name,over,coef,pullback", CASES)
-def test_graph_replay_matches_eager(name, over, coef, pullback):
+@pytest.mark.parametrize("name,over,coef,pullback,flush", CASES)
+def test_graph_replay_matches_eager(name, over, coef, pullback, flush):
     import synth
     from ssm_decode_amd import abi, feed
     cfg = CONFIGS[name].with_(name=name + "_graph", **over)
-    print(f"\n[graph] {cfg.name} B={cfg.batch} W={cfg.window} {coef} {pullback}", flush=True)
+    print(f"\n[graph] {cfg.name} B={cfg.batch} W={cfg.window} {coef} {pullback} {flush}", flush=True)
     li = synth.make_layer_inputs(cfg)
     lay = feed.make_layer(cfg, li, coef=coef, pullback=pullback)
     feed.fill_state(lay, cfg)
@@ -57,15 +62,33 @@ def test_graph_replay_matches_eager(name, over, coef, pullback):
         for st in steps:
             st.o.zero_()
 
-    def run(stream):
-        for st in steps:
+    # the sequences whose window closes at step t, from the initial fills
+    import numpy as np
+    c0 = np.asarray(li.count0)
+    lists = [torch.from_numpy(np.nonzero((c0[:, 0] + t + 1) % cfg.window == 0)[0].astype(np.int32)).cuda()
+             for t in range(K)]
+
+    def run(stream, mode=flush):
+        for t, st in enumerate(steps):
             assert lay.read(st, stream=stream) == 0
-            assert lay.flush(st, abi.SKSSM_FLUSH_DUE, stream=stream) == 0
+            if mode == "list":
+                assert lay.flush_seqs(st, lists[t], stream=stream) == 0
+            else:
+                assert lay.flush(st, abi.SKSSM_FLUSH_DUE, stream=stream) == 0
 
     run(None)                                  # eager
     torch.cuda.synchronize()
     eager_o = [st.o.clone() for st in steps]
     eager_b = {n: b.clone() for n, b in _buffers(lay).items()}
+    if flush == "list":                        # the lists name exactly the due sequences
+        assert (c0 == c0[:, :1]).all()
+        restore()
+        run(None, "due")
+        torch.cuda.synchronize()
+        for t, st in enumerate(steps):
+            assert torch.equal(st.o, eager_o[t]), ("due vs list", t)
+        for n, b in _buffers(lay).items():
+            assert torch.equal(b, eager_b[n]), ("due vs list", n)
 
     restore()
     torch.cuda.synchronize()
