@@ -31,13 +31,32 @@ def _compile(src: str, extra=(), tag: str = "") -> str:
     return obj
 
 
-def build(jobs: int = 4, extra=(), out: str = LIB) -> str:
+def _stale(src: str, tag: str) -> bool:
+    """An object is stale when it is missing or older than its source or any
+    header it may include (the csrc headers and include/sketchssm.h)."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src), os.path.join(ROOT, "include", "sketchssm.h")]
+    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(jobs: int = 4, extra=(), out: str = LIB, incremental: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library.
-    extra: additional compiler flags (e.g. -D tuning macros); out: library path."""
+    extra: additional compiler flags (e.g. -D tuning macros); out: library path;
+    incremental: recompile only the objects older than their sources."""
     os.makedirs(BUILD, exist_ok=True)
     tag = "" if out == LIB else "_" + os.path.basename(out).replace(".so", "")
+
+    def obj_of(src):
+        if incremental and not extra and not _stale(src, tag):
+            return os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+        return _compile(src, extra, tag)
+
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, extra, tag), SOURCES))
+        objs = list(ex.map(obj_of, SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,5 +67,5 @@ def build(jobs: int = 4, extra=(), out: str = LIB) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(incremental="--incremental" in sys.argv))
     sys.exit(0)

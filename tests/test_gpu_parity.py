@@ -138,11 +138,69 @@ def test_full_kda_b256():
 
 @pytest.mark.parametrize("idx", list(range(9)))
 def test_full_stress_sweep(idx):
+    """Every sweep point at batch 1024 for the workload's full 512 steps
+    (16 to 64 windows), on sampled tiles."""
     from tests.gpu_parity import sample_tiles
     cfg = sweep_configs()[idx]
-    steps = cfg.steps if (cfg.window, cfg.mean_rank) == (16, 8) else 2 * cfg.window + 7
     tiles = sample_tiles(cfg, 4, 3, seed=cfg.seed)
-    run(cfg, "sketch", steps=steps, tiles=tiles, numpy_all=False)
+    rep = run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False)
+    assert rep.steps == 512 and rep.flushes >= cfg.steps // cfg.window
+
+
+# ------------- the flush of listed sequences (sketchssm_flush_seqs) vs oracle
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
+def test_flush_list_small_batch(name):
+    cfg = CONFIGS[name].with_(name=name + "_list", batch=5, ragged=True, steps=40)
+    run(cfg, "sketch", flush="list")
+
+
+def test_flush_list_stress_w32():
+    """The batch-1024 W = 32 stress point, flushed through the caller's
+    list of due sequences, for the full 512 steps on sampled tiles."""
+    from tests.gpu_parity import sample_tiles
+    cfg = [c for c in sweep_configs() if (c.window, c.mean_rank) == (32, 8)][0]
+    tiles = sample_tiles(cfg, 4, 3, seed=cfg.seed + 1)
+    run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False, flush="list")
+
+
+# ------------- the delta rule's 32-slot chunked flush at the real head shape
+@pytest.mark.parametrize("flush", ["due", "list"])
+@pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
+def test_delta_rule_w32_real_heads(name, flush):
+    """dk = dv = 128 with W = 32: the chunked flush applies 32 entries (two
+    16-entry blocks of the triangular system), every tile, ragged phases,
+    2W + 3 steps."""
+    cfg = CONFIGS[name].with_(name=name + "_w32", batch=3, window=32, ragged=True, steps=67)
+    run(cfg, "sketch", flush=flush)
+
+
+def test_delta_rule_w32_full_batch():
+    """The same at the full batch of 256 (aligned), on sampled tiles."""
+    from tests.gpu_parity import sample_tiles
+    for name in ("gdn_b256", "kda_b256"):
+        cfg = CONFIGS[name].with_(name=name + "_w32_full", window=32, steps=70)
+        run(cfg, "sketch", tiles=sample_tiles(cfg, 4, 4, seed=cfg.seed), numpy_all=False)
+
+
+# ---------------------------- the checker itself catches a one-tile mistake
+def _planted(plant, **kw):
+    cfg = CONFIGS["m2_b320"].with_(name="m2_planted", batch=4, steps=16, **kw)
+    return run(cfg, "sketch", plant=plant, log=False)
+
+
+def test_checker_catches_one_tile_mistakes():
+    """A mistake planted on the CPU in the oracle's expected values of one
+    tile of 512 (5% in one output vector, 5% in one sketch, 6e-5 in one
+    state) stays under the pooled gate but fails the per-tile gate; without
+    it the same run passes."""
+    base = _planted({})
+    assert base.tile_o < 0.01 and base.tile_S < 1e-5 and base.tile_U < 0.01
+    with pytest.raises(AssertionError, match="per-tile rel-L2\\(o\\)"):
+        _planted({"o": (3, 77, 0.05)})
+    with pytest.raises(AssertionError, match="per-tile U"):
+        _planted({"U": (0, 300, 0.05)})
+    with pytest.raises(AssertionError, match="per-tile S"):
+        _planted({"S": (0, 5, 6e-5)})
 
 
 @pytest.mark.parametrize("name,W", [("m2_b320", 16), ("m2_b320", 32), ("gdn_b256", 16), ("kda_b256", 32)])
