@@ -33,7 +33,10 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=160, help="timed decode steps (per layer)")
+    ap.add_argument("--steps", type=int, default=160,
+                    help="timed decode steps per layer (rounded up to whole windows)")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed replays of the captured steps (the median is reported)")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_b320")
     ap.add_argument("--layers", type=int, default=0, help="rotated layer instances (0: auto)")
@@ -128,7 +131,11 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     phase = int(li.phase[0])
     ragged = cfg.ragged
-    K = args.steps
+    # the timed steps are whole windows: every window of a layer is one flush
+    # and W - 1 reads, so the per-step figure is W-amortised exactly
+    K_req = args.steps
+    K = max(W, -(-K_req // W) * W)
+    REPS = max(5, args.reps)
     # listed flush: the sequences whose window closes at step t (t mod W),
     # from each sequence's initial ring fill; device-resident for the graph
     flush_lists = None
@@ -139,8 +146,10 @@ def main():
                        for r in range(W)]
 
     def measure(layers):
-        """Event-timed eager kernels over two windows, then exactly K steps
-        captured in one HIP graph and timed around its replay."""
+        """Event-timed eager kernels over two windows, then K steps (whole
+        windows) captured in one HIP graph, replayed REPS times back to back
+        (each replay starts at a window boundary), HIP events around every
+        replay; the median replay gives the step time."""
 
         def one_step(t, ev=None, stream_handle=None):
             sh_ = sh if stream_handle is None else stream_handle
@@ -194,10 +203,11 @@ def main():
         read_us = [a.elapsed_time(b) * 1000 for a, b in ev["read"]]
         flush_us = [a.elapsed_time(b) * 1000 for a, b in ev["flush"]]
 
-        # the timed steps: exactly K steps (every layer's read, and its flush
-        # when a window closes) captured in one HIP graph and replayed once,
-        # so that host launch overhead is not timed; the device ring counts
-        # advance exactly as in eager execution
+        # the timed steps: K steps, whole windows (every layer's read, and its
+        # flush when a window closes) captured in one HIP graph, so that host
+        # launch overhead is not timed; the device ring counts advance exactly
+        # as in eager execution, and since K is a multiple of W every replay
+        # starts at the same window phase
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             capture_handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -206,19 +216,20 @@ def main():
         torch.cuda.synchronize()
         graph.replay()                      # warm replay
         torch.cuda.synchronize()
-        t += K
-        t = realign(t)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(REPS)]
+        for a, b in evs:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
         torch.cuda.synchronize()
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        graph.replay()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        total_ms = start.elapsed_time(stop)
+        reps_ms = [a.elapsed_time(b) for a, b in evs]
         del graph
         err = max(lay.error_word() for lay in layers)
         assert err == 0, f"device error word {err}"
-        return {"us_per_step": total_ms * 1000.0 / (K * L),
+        med = float(np.median(reps_ms))
+        return {"us_per_step": med * 1000.0 / (K * L),
+                "reps_us_per_step": [round(x * 1000.0 / (K * L), 3) for x in reps_ms],
                 "flush_avg": float(np.mean(flush_us)) if flush_us else float("nan"),
                 "flush_n": len(flush_us), "read_avg": float(np.mean(read_us)), "read_n": len(read_us)}
 
@@ -227,7 +238,8 @@ def main():
     m = measure(layers)
     us_per_step, flush_avg, read_avg = m["us_per_step"], m["flush_avg"], m["read_avg"]
     flush_us, read_us = [0] * m["flush_n"], [0] * m["read_n"]
-    log(f"[bench] sketch: {us_per_step:.2f} us/step/layer (graph of {K} steps x {L} layers); "
+    log(f"[bench] sketch: {us_per_step:.2f} us/step/layer, median of {REPS} replays "
+        f"{m['reps_us_per_step']} (graph of {K} steps = {K // W} windows x {L} layers); "
         f"flush avg {flush_avg:.1f} us ({len(flush_us)} launches); read avg {read_avg:.2f} us")
 
     achieved_gbs = lb.per_step / (us_per_step * 1e-6) / 1e9
@@ -236,36 +248,44 @@ def main():
         (lb.flush_launch - lb.basis) / W + lb.basis
     flush_gbs = flush_bytes / (flush_avg * 1e-6) / 1e9
     read_gbs = lb.read_launch_avg / (read_avg * 1e-6) / 1e9
-    windows_exact = ragged or K % W == 0
+    windows_exact = K % W == 0
 
     # ------------------------------------------------ GPU baselines
     baselines = None
     if not args.no_baselines:
         lay = layers[0]
+
+        def graph_us(call, n):
+            """n steps of one call captured in a HIP graph (as the sketch path
+            is timed), replayed REPS times; median µs per step."""
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                hc = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for i in range(n):
+                    assert call(lay.layer_struct, lay.buffers_struct, steps_structs[i % P][0], hc) == 0
+            torch.cuda.synchronize()
+            g.replay()                          # warm replay
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(REPS)]
+            for a, b in evs:
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            del g
+            return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1000 / n
+
         # standard full-state step
-        nb = max(W, 16)
-        for i in range(4):
-            abi.sketchssm_full_step(lay.layer_struct, lay.buffers_struct, steps_structs[i % P][0], sh)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(nb):
-            assert abi.sketchssm_full_step(lay.layer_struct, lay.buffers_struct,
-                                           steps_structs[i % P][0], sh) == 0
-        b.record(stream)
-        torch.cuda.synchronize()
-        full_us = a.elapsed_time(b) * 1000 / nb
-        # ReplaySSM over whole windows (its ring restarts from an empty window)
+        full_us = graph_us(abi.sketchssm_full_step, W)
+        # ReplaySSM over whole windows (its ring restarts from an empty window
+        # and is empty again after every replay)
         lay.count.zero_()
         torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(nb):
-            assert abi.sketchssm_replay_step(lay.layer_struct, lay.buffers_struct,
-                                             steps_structs[i % P][0], sh) == 0
-        b.record(stream)
-        torch.cuda.synchronize()
-        replay_us = a.elapsed_time(b) * 1000 / nb
+        replay_us = graph_us(abi.sketchssm_replay_step, W)
+        assert lay.error_word() == 0
         baselines = {
+            "timing": f"{W} steps (one window) captured in a HIP graph, median of {REPS} replays",
             "full_step_us": round(full_us, 2),
             "full_step_gbs": round(lb.full_step / (full_us * 1e-6) / 1e9, 1),
             "replay_step_us": round(replay_us, 2),
@@ -379,6 +399,10 @@ def main():
         "unit": "us/step",
         "n_gpus": 1,
         "steps": K,
+        "steps_requested": K_req,
+        "windows": K // W,
+        "reps": REPS,
+        "reps_us_per_step": m["reps_us_per_step"],
         "warmup": args.warmup,
         "ms_per_step": round(us_per_step / 1000.0, 6),
         "higher_is_better": False,
@@ -406,8 +430,9 @@ def main():
             "read_bytes_avg": int(round(lb.read_launch_avg)), "read_gbs": round(read_gbs, 1),
             "timing": "eager launches bracketed by HIP events on the launch stream",
         },
-        "step_timing": "the K timed steps captured in one HIP graph and replayed; "
-                       "HIP events around the replay",
+        "step_timing": f"{K} steps ({K // W} whole windows) x {L} rotated layers captured in one "
+                       f"HIP graph, replayed {REPS} times back to back with HIP events around each "
+                       "replay; value = the median replay / (steps x layers)",
         "roofline": {
             "bound": "hbm", "kernel": "flush", "achieved": round(flush_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
@@ -495,10 +520,39 @@ def sketch_error(cfg, li, src, pool, steps, coef="fixed"):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, li, n_seq, windows):
     """The oracle, as it stands, on a bounded sample: n_seq sequences x every
-    head of the workload, whole windows (prime excluded), on all host cores;
-    scaled to the whole batch per layer step."""
+    head of the workload, whole windows (prime excluded), on all host cores
+    (OpenMP over tiles), then a smaller sample on one core; both scaled to
+    the whole batch per layer step."""
+    import oracle
+    allc = _cpu_run(cfg, li, n_seq, windows)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        n1, w1 = max(1, n_seq // 16), max(1, windows // 4)
+        one = _cpu_run(cfg, li, n1, w1)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": allc["value"], "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": allc["sample"], "seconds": allc["seconds"],
+            "value_1core": one["value"], "sample_1core": one["sample"], "seconds_1core": one["seconds"],
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _cpu_run(cfg, li, n_seq, windows):
     import numpy as np
     import oracle
     import synth
@@ -522,7 +576,7 @@ def cpu_baseline(cfg, li, n_seq, windows):
         dt += time.perf_counter() - t0
     frac = cfg.batch / n_seq
     us = dt / nsteps * frac * 1e6
-    return {"value": round(us, 1), "unit": "us/step", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(us, 1),
             "sample": f"{n_seq} of {cfg.batch} sequences x {cfg.heads} heads, {windows} windows of "
                       f"{cfg.window} steps ({dt:.1f} s), scaled to the batch",
             "seconds": round(dt, 2)}
