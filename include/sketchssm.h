@@ -35,8 +35,9 @@
  *   - Every pointer inside sketchssm_buffers / sketchssm_step is a DEVICE
  *     pointer owned by the caller.  sketchssm_layer and its rank_offsets_host
  *     table are HOST memory, read during the call only and never retained.
- *   - The library allocates nothing, keeps no state between calls and never
- *     synchronises: every call only enqueues kernels on the caller's HIP
+ *   - The library allocates nothing, keeps no state between calls (except
+ *     the per-device address of sketchssm_read_noalloc's scratch array) and
+ *     never synchronises: every call only enqueues kernels on the caller's HIP
  *     stream (NULL = the default stream).  Buffers must not be reused until
  *     stream order guarantees completion.  Calls on different layers may run
  *     concurrently on different streams; calls on one layer must be ordered.
@@ -94,6 +95,12 @@ extern "C" {
 #define SKSSM_EDTYPE -3  /* unsupported dtype combination */
 #define SKSSM_EFLAG -4   /* unknown flag or coefficient-map mode */
 #define SKSSM_ELAUNCH -5 /* kernel launch failed */
+#define SKSSM_ESCRATCH -6 /* sketchssm_read_noalloc: the layer needs more scratch than the
+                             library's array holds (SKSSM_NOALLOC_SCRATCH_BYTES) */
+
+/* size of the device array that sketchssm_read_noalloc uses as its workspace
+ * (16 MiB; one per GPU the library runs on, held until the process ends) */
+#define SKSSM_NOALLOC_SCRATCH_BYTES 16777216
 
 /* bits OR-ed into *err by the kernels */
 #define SKSSM_ERRBIT_COUNT 1  /* count outside [0, W] (or == W at a read) */
@@ -233,6 +240,23 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
  * (int32), passed from the read's main launch to the launch that reads the
  * state copies.  The caller allocates it; the library never does. */
 int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
+
+/* sketchssm_read for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics, kernels and results as sketchssm_read, except
+ * that bufs->work is ignored: the workspace is a device array of the library
+ * (SKSSM_NOALLOC_SCRATCH_BYTES, one per GPU, resolved on the first call on
+ * each device).  The call allocates nothing and never synchronises.
+ * Returns SKSSM_ESCRATCH, launching nothing, when sketchssm_workspace_bytes
+ * of the layer exceeds SKSSM_NOALLOC_SCRATCH_BYTES (at dk = 128 this holds,
+ * e.g., a Mamba-2 layer of 1024 sequences with 2048 sketch rows and W = 32).
+ * Every call on one GPU shares that GPU's array, whatever the layer or
+ * stream: calls that may overlap on one GPU (two streams, two threads) race
+ * and must be ordered by the caller.  The array keeps the last call's
+ * contents; every value a call reads from it is written earlier in the same
+ * call, so nothing needs clearing. */
+int sketchssm_read_noalloc(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                           const sketchssm_step* step, void* hip_stream);
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int sketchssm_version(void);

@@ -21,10 +21,13 @@ SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL = 0, 1
 SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
 SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY = 0, 1
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5
+SKSSM_ESCRATCH = -6
+SKSSM_NOALLOC_SCRATCH_BYTES = 16777216
 SKSSM_ERRBIT_COUNT, SKSSM_ERRBIT_GROUP, SKSSM_ERRBIT_SEQ = 1, 2, 4
 
 ENTRY_POINTS = ("sketchssm_read", "sketchssm_flush", "sketchssm_flush_seqs", "sketchssm_full_step",
-                "sketchssm_replay_step", "sketchssm_workspace_bytes", "sketchssm_version")
+                "sketchssm_replay_step", "sketchssm_workspace_bytes", "sketchssm_read_noalloc",
+                "sketchssm_version")
 
 
 class sketchssm_layer(C.Structure):
@@ -60,7 +63,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                                "(or python ssm_decode_amd/build.py) first")
         lib = C.CDLL(path)
         L, Bf, St = C.POINTER(sketchssm_layer), C.POINTER(sketchssm_buffers), C.POINTER(sketchssm_step)
-        for name in ("sketchssm_read", "sketchssm_full_step", "sketchssm_replay_step"):
+        for name in ("sketchssm_read", "sketchssm_read_noalloc", "sketchssm_full_step",
+                     "sketchssm_replay_step"):
             fn = getattr(lib, name)
             fn.argtypes = [L, Bf, St, C.c_void_p]
             fn.restype = C.c_int
@@ -87,6 +91,13 @@ def _ref(x, ty):
 def sketchssm_read(layer, bufs, step, stream=None) -> int:
     return load().sketchssm_read(_ref(layer, sketchssm_layer), _ref(bufs, sketchssm_buffers),
                                  _ref(step, sketchssm_step), stream)
+
+
+def sketchssm_read_noalloc(layer, bufs, step, stream=None) -> int:
+    """sketchssm_read with the library's own scratch array as the workspace
+    (bufs.work is ignored; nothing is allocated)."""
+    return load().sketchssm_read_noalloc(_ref(layer, sketchssm_layer), _ref(bufs, sketchssm_buffers),
+                                         _ref(step, sketchssm_step), stream)
 
 
 def sketchssm_flush(layer, bufs, step, flags, stream=None) -> int:

@@ -18,7 +18,7 @@ ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
-SOURCES = ["sk_api.cpp", "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip"]
+SOURCES = ["sk_api.cpp", "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip", "sk_noalloc.hip"]
 
 
 def _compile(src: str, extra=(), tag: str = "") -> str:

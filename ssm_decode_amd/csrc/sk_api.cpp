@@ -9,6 +9,10 @@
 #include "sketchssm.h"
 #include "sk_params.hpp"
 
+namespace sk {
+int noalloc_scratch(void** out);   // sk_noalloc.hip
+}
+
 namespace {
 
 constexpr int kMaxW = 32;
@@ -183,6 +187,29 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
     const Needs nd{false, true, false, true, true, true, true, true, true, true, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     return dispatch(layer, sk::MODE_READ, make_params(layer, bufs, step), hip_stream);
+  } catch (...) {
+    return SKSSM_ELAUNCH;
+  }
+}
+
+int sketchssm_read_noalloc(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
+                           const sketchssm_step* step, void* hip_stream) {
+  try {
+    int rc = check_layer(layer);
+    if (rc) return rc;
+    const int64_t need = workspace_bytes(layer);
+    if (need > (int64_t)SKSSM_NOALLOC_SCRATCH_BYTES) return SKSSM_ESCRATCH;
+    // (bufs->work is not used: the workspace is the library's scratch array)
+    const Needs nd{false, true, false, true, true, true, true, true, true, false, true};
+    if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    sk::Params p = make_params(layer, bufs, step);
+    p.work = nullptr;
+    if (need > 0 && layer->batch > 0) {
+      void* scratch = nullptr;
+      if ((rc = sk::noalloc_scratch(&scratch))) return rc;
+      p.work = scratch;
+    }
+    return dispatch(layer, sk::MODE_READ, p, hip_stream);
   } catch (...) {
     return SKSSM_ELAUNCH;
   }

@@ -138,6 +138,10 @@ class DecodeLayer:
     def read(self, step: DeviceStep, stream=None) -> int:
         return abi.sketchssm_read(self._layer, self._bufs, step.struct(), self._stream(stream))
 
+    def read_noalloc(self, step: DeviceStep, stream=None) -> int:
+        """The read with the library's scratch array as its workspace."""
+        return abi.sketchssm_read_noalloc(self._layer, self._bufs, step.struct(), self._stream(stream))
+
     def flush(self, step: Optional[DeviceStep], flags: int = abi.SKSSM_FLUSH_DUE, stream=None) -> int:
         st = None if step is None else step.struct()
         return abi.sketchssm_flush(self._layer, self._bufs, st, flags, self._stream(stream))

@@ -285,3 +285,26 @@ def test_flush_seqs_binding_rejects_host_or_wrong_lists():
         _Stub().flush_seqs(None, torch.zeros(2, dtype=torch.int64))
     with pytest.raises(ValueError):
         _Stub().flush_seqs(None, torch.zeros(4, dtype=torch.int32)[::2])
+
+
+def test_read_noalloc_validation(lib):
+    """The read without a workspace argument validates like the read, ignores
+    bufs.work, and refuses (SKSSM_ESCRATCH, nothing launched) a layer whose
+    workspace exceeds the library's scratch array; batch 0 is a no-op that
+    does not touch the device."""
+    L0 = _layer(OK_OFF, batch=0)
+    assert abi.sketchssm_read_noalloc(L0, _bufs(work=None), _step()) == 0
+    L = _layer(OK_OFF)
+    assert abi.sketchssm_read_noalloc(L, _bufs(C=FAKE + 8), _step()) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read_noalloc(L, _bufs(), None) == abi.SKSSM_EINVAL
+    assert abi.sketchssm_read_noalloc(_layer(OK_OFF, W=33), _bufs(), _step()) == abi.SKSSM_EDIM
+    # the largest Mamba-2 layer that fits, and one sequence more: the query in
+    # every head's basis alone is 4 B x R per sequence
+    off = np.concatenate([[0], np.cumsum(np.full(128, 16))]).astype(np.int32)   # R = 2048
+    cap = abi.SKSSM_NOALLOC_SCRATCH_BYTES
+    Bfit = max(b for b in range(1, 4096) if _m2_work_bytes(b, 2048, 8, 32) <= cap)
+    Lbig = _layer(off, batch=Bfit + 1, heads=128, groups=8, dk=128, dv=64, W=32)
+    assert abi.sketchssm_workspace_bytes(Lbig) > cap
+    assert abi.sketchssm_read_noalloc(Lbig, _bufs(), _step()) == abi.SKSSM_ESCRATCH
+    assert abi.sketchssm_read_noalloc(Lbig, _bufs(work=None), _step()) == abi.SKSSM_ESCRATCH
+    assert Bfit >= 1024                   # the batch-1024 stress layers fit
