@@ -20,6 +20,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sketchssm_oracle.c")
 _LIB = os.path.join(_HERE, "_build", "libsketchssm_oracle.so")
+# another build of the same source (the sanitizer test loads an instrumented one)
+_LIB = os.environ.get("SKSSM_ORACLE_LIB", _LIB)
 
 FAMILY = {"mamba2": 0, "gdn": 1, "kda": 2}
 STORE = {"exact": 0, "f32": 1, "bf16": 2}
@@ -28,15 +30,17 @@ PULLBACK = {"serial": 0, "wy": 1}
 ERR_COUNT = 1
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = True, out: str = None, extra=()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math); out and extra
+    build another copy (e.g. with sanitizers) at another path."""
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-                               "-Wall", "-Wno-unknown-pragmas", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               "-Wall", "-Wno-unknown-pragmas"] + list(extra) + [_SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _Layer(C.Structure):
