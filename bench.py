@@ -49,6 +49,8 @@ def parse():
                     help="skip the run with dense-fallback heads")
     ap.add_argument("--flush-list", action="store_true",
                     help="ragged phase: flush through sketchssm_flush_seqs with each step's due sequences")
+    ap.add_argument("--flush-scan", action="store_true",
+                    help="flush with SKSSM_FLUSH_DUE_SCAN (the due tiles listed on the device)")
     ap.add_argument("--no-wy", action="store_true",
                     help="skip the GDN/KDA run with the triangular-system pull-back")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
@@ -174,7 +176,8 @@ def main():
                                                       int(dl.numel()), sh_)
                     else:
                         rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
-                                                 abi.SKSSM_FLUSH_DUE, sh_)
+                                                 abi.SKSSM_FLUSH_DUE_SCAN if args.flush_scan
+                                                 else abi.SKSSM_FLUSH_DUE, sh_)
                     if ev is not None:
                         ev["flush"][-1][1].record(stream)
                     assert rc == 0
@@ -359,17 +362,21 @@ def main():
     # pull-back (a Mamba-2 effective query is a decay only: no such run)
     wy_block = None
     if not args.no_wy and cfg.family != "mamba2":
-        torch.cuda.empty_cache()
-        layers = make_layers("fixed", pullback="wy")
-        mw = measure(layers)
-        wy_block = {
-            "us_per_step": round(mw["us_per_step"], 3),
-            "achieved_gbs": round(lb.per_step / (mw["us_per_step"] * 1e-6) / 1e9, 1),
-            "flush_us": round(mw["flush_avg"], 2), "read_us": round(mw["read_avg"], 2),
-            "us_per_step_serial": round(us_per_step, 3), "read_us_serial": round(read_avg, 2),
-        }
-        log(f"[bench] triangular-system pull-back: {wy_block}")
-        del layers
+        wy_block = {"us_per_step_serial": round(us_per_step, 3), "read_us_serial": round(read_avg, 2)}
+        # the triangular-system pull-back, and the same with projected
+        # per-slot factors (the algorithmic bytes are those of the serial
+        # form; the factors add 64 B per buffered slot and tile)
+        for pb in ("wy", "proj"):
+            torch.cuda.empty_cache()
+            layers = make_layers("fixed", pullback=pb)
+            mw = measure(layers)
+            wy_block[pb] = {
+                "us_per_step": round(mw["us_per_step"], 3),
+                "achieved_gbs": round(lb.per_step / (mw["us_per_step"] * 1e-6) / 1e9, 1),
+                "flush_us": round(mw["flush_avg"], 2), "read_us": round(mw["read_avg"], 2),
+            }
+            del layers
+        log(f"[bench] triangular-system pull-back (wy) and projected factors (proj): {wy_block}")
 
     # ------------------------------------------ copy-bandwidth reference
     nbytes = 2 * 2 ** 30
@@ -415,7 +422,9 @@ def main():
             "qk_groups": cfg.qk_groups, "dk": cfg.dk, "dv": cfg.dv, "window": W,
             "mean_rank": cfg.mean_rank, "state": "f32", "act": cfg.act, "sketch": cfg.sketch,
             "layers_rotated": L, "windows_exact": windows_exact,
-            "flush": "listed sequences (sketchssm_flush_seqs)" if flush_lists is not None else "due flag",
+            "flush": ("listed sequences (sketchssm_flush_seqs)" if flush_lists is not None else
+                      "due tiles listed on the device (SKSSM_FLUSH_DUE_SCAN)" if args.flush_scan
+                      else "due flag"),
         },
         "achieved_gbs": round(achieved_gbs, 1),
         "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),

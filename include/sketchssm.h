@@ -83,10 +83,21 @@ extern "C" {
 #define SKSSM_PULLBACK_WY 1     /* every buffered slot's coefficient from one triangular
                                    system over the slots (paper App. C.1), then q~ and
                                    the buffered term as sums over the slots */
+#define SKSSM_PULLBACK_PROJ 2   /* the coefficients of SKSSM_PULLBACK_WY, with C q~ formed
+                                   from per-slot factors projected through the coefficient
+                                   map (paper App. C.2): the read that appends slot l stores
+                                   P_l = C_h (Gamma_l (.) k_l) in bufs->ring_pc (Gamma_l:
+                                   the product of the decays of slots 0..l), and
+                                   C q~ = C_h (Gamma_n0 (.) q) - sum_l beta_l d_l P_l.
+                                   Every non-flush step of such a layer is a
+                                   sketchssm_read (replay steps do not store factors). */
 
 /* flush flags */
 #define SKSSM_FLUSH_DUE 0 /* flush tiles whose ring holds W entries */
 #define SKSSM_FLUSH_ALL 1 /* flush every tile (prime U, or retire sequences) */
+#define SKSSM_FLUSH_DUE_SCAN 2 /* as SKSSM_FLUSH_DUE, with the due tiles first listed on
+                                  the device (in bufs->work), so that a ragged window phase
+                                  launches workgroups for the due tiles only */
 
 /* return codes */
 #define SKSSM_OK 0
@@ -105,7 +116,8 @@ extern "C" {
 /* bits OR-ed into *err by the kernels */
 #define SKSSM_ERRBIT_COUNT 1  /* count outside [0, W] (or == W at a read) */
 #define SKSSM_ERRBIT_GROUP 2  /* Mamba-2 heads of one B/C group disagree on count */
-#define SKSSM_ERRBIT_SEQ 4    /* sketchssm_flush_seqs: a listed index outside [0, batch) */
+#define SKSSM_ERRBIT_SEQ 4    /* sketchssm_flush_seqs: a listed index outside [0, batch),
+                                 or a tile claimed twice (a sequence listed twice) */
 
 /* Supported shapes: (dk, dv) in {(16,32), (64,64), (128,64), (128,128)};
  * 1 <= W <= 32; 0 <= r_h <= min(dk, 16), except r_h <= dk when dk == 16
@@ -128,7 +140,7 @@ typedef struct {
   float coef_ridge;          /* SKSSM_COEF_STATE: ridge relative to the mean eigenvalue of
                                 the sketch's Gram matrix, lambda = coef_ridge * trace(G) / r_h;
                                 finite and > 0 (ignored for SKSSM_COEF_FIXED) */
-  int32_t pullback;          /* SKSSM_PULLBACK_SERIAL or SKSSM_PULLBACK_WY (non-flush reads) */
+  int32_t pullback;          /* SKSSM_PULLBACK_SERIAL, _WY or _PROJ (non-flush reads) */
 } sketchssm_layer;
 
 typedef struct {
@@ -159,6 +171,8 @@ typedef struct {
                                 written by their flush, read by their non-flush reads.  NULL
                                 allowed when D = 0.  (Compact: a [B][H] layout would put the
                                 few dense tiles at strides that load a few memory channels.) */
+  float* ring_pc;            /* GDN/KDA with SKSSM_PULLBACK_PROJ: [B][H][W][16] fp32, slot l
+                                of tile (b, h) holds P_l (r_h entries); NULL otherwise */
 } sketchssm_buffers;
 
 typedef struct {             /* one decode step */
@@ -195,7 +209,15 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * fp32 from the sketch rows as stored (rounded to the sketch dtype) and the
  * updated state: G = U_h U_h^T (r_h x r_h), Y = U_h S^T (r_h x dk),
  * C = (G + lambda I)^{-1} Y, lambda = coef_ridge * trace(G) / r_h, stored in
- * the sketch dtype (C = 0 when the sketch is zero). */
+ * the sketch dtype (C = 0 when the sketch is zero).
+ * SKSSM_FLUSH_DUE_SCAN (paper App. B: each sequence flushes when its own
+ * window fills): the same result as SKSSM_FLUSH_DUE, for callers that do not
+ * track window phases.  A first launch lists the tiles whose count is W in
+ * bufs->work (sketchssm_workspace_bytes; 16-byte aligned) and reports counts
+ * outside [0, W] (SKSSM_ERRBIT_COUNT, tile untouched); the flush then runs a
+ * grid of about one round of resident workgroups over the listed tiles, so
+ * that a ragged phase (about batch / W sequences due a step) does not pay a
+ * workgroup per tile of the batch. */
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,
                     void* hip_stream);
@@ -207,10 +229,13 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * about batch / W sequences are due per step, and the due-flag flush pays
  * for a workgroup per tile of the whole batch.  seqs: DEVICE array of nseq
  * distinct sequence indices (int32, 4-byte aligned), 0 <= nseq <= batch.
- * A listed tile whose count is not W is left alone; an index outside
- * [0, batch) sets SKSSM_ERRBIT_SEQ and is skipped.  Two equal indices in one
- * list would flush the same tiles at once: the caller keeps them distinct.
- * nseq = 0 launches nothing. */
+ * A listed tile whose count is in [0, W) is left alone; a count outside
+ * [0, W] sets SKSSM_ERRBIT_COUNT; an index outside [0, batch) sets
+ * SKSSM_ERRBIT_SEQ and is skipped.  Each tile is claimed before it is
+ * flushed (its count goes from W to W + 1 until the flush stores 0), so a
+ * sequence listed twice is flushed once, and the second claim of a tile
+ * that is still being flushed sets SKSSM_ERRBIT_SEQ.  nseq = 0 launches
+ * nothing. */
 int sketchssm_flush_seqs(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                          const sketchssm_step* step /* NULL: no output */, const int32_t* seqs,
                          int32_t nseq, void* hip_stream);
@@ -228,17 +253,22 @@ int sketchssm_full_step(const sketchssm_layer* layer, const sketchssm_buffers* b
 int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                           const sketchssm_step* step, void* hip_stream);
 
-/* Bytes of the workspace bufs->work that sketchssm_read needs for this layer
- * (0 when it needs none), or a negative SKSSM_E* code for an invalid layer.
- * Mamba-2 uses it for what the heads of a B/C group share at a step: the
- * query's coordinates in every head's sketch basis, C_h q (B x R fp32; the
- * decay factor of the pulled-back query is applied afterwards), the dot
- * products of the query with the group's buffered keys (B x G x W fp32) and
- * the group's checked ring fill (B x G int32).  GDN and KDA use it only when
- * the layer has dense-fallback heads: per (sequence, dense head) the
- * pulled-back query (dk fp32), the buffered term (dv fp32) and a flag
- * (int32), passed from the read's main launch to the launch that reads the
- * state copies.  The caller allocates it; the library never does. */
+/* Bytes of the workspace bufs->work for this layer, or a negative SKSSM_E*
+ * code for an invalid layer: the larger of what sketchssm_read and
+ * sketchssm_flush with SKSSM_FLUSH_DUE_SCAN need (a call uses the workspace
+ * only while it runs, and calls on one layer are ordered, so both share it).
+ * The read needs it (and checks bufs->work) only for these layers:
+ * Mamba-2, for what the heads of a B/C group share at a step: the query's
+ * coordinates in every head's sketch basis, C_h q (B x R fp32; the decay
+ * factor of the pulled-back query is applied afterwards), the dot products
+ * of the query with the group's buffered keys (B x G x W fp32) and the
+ * group's checked ring fill (B x G int32); GDN and KDA with dense-fallback
+ * heads: per (sequence, dense head) the pulled-back query (dk fp32), the
+ * buffered term (dv fp32) and a flag (int32), passed from the read's main
+ * launch to the launch that reads the state copies.  The scan flush lists
+ * the due tiles: per region of 1024 tiles (b * H + h) its number of due
+ * tiles, then its list (int32).  The caller allocates it; the library never
+ * does. */
 int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
 
 /* sketchssm_read for callers that cannot allocate device memory: code under

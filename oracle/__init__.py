@@ -26,7 +26,7 @@ _LIB = os.environ.get("SKSSM_ORACLE_LIB", _LIB)
 FAMILY = {"mamba2": 0, "gdn": 1, "kda": 2}
 STORE = {"exact": 0, "f32": 1, "bf16": 2}
 COEF = {"fixed": 0, "state": 1}
-PULLBACK = {"serial": 0, "wy": 1}
+PULLBACK = {"serial": 0, "wy": 1, "proj": 2}
 ERR_COUNT = 1
 
 
@@ -57,7 +57,7 @@ _IP = C.POINTER(C.c_int)
 class _Tiles(C.Structure):
     _fields_ = [("n", C.c_int), ("rank", _IP), ("S", _DP), ("U", _DP), ("Pt", _DP),
                 ("C", _DP), ("A", _DP), ("rk", _DP), ("rv", _DP), ("rg", _DP),
-                ("rb", _DP), ("count", _IP), ("Sc", _DP)]
+                ("rb", _DP), ("count", _IP), ("Sc", _DP), ("rp", _DP)]
 
 
 class _Step(C.Structure):
@@ -117,8 +117,11 @@ class OracleLayer:
     write each tile's own map from its new state (Cmap is then ignored) with
     the relative ridge ``ridge``; the map is stored in the sketch dtype.
     pullback: how the sketched read evaluates the effective query and the
-    buffered term, "serial" (one transition at a time) or "wy" (every slot's
-    coefficient at once from a triangular system, paper App. C.1).
+    buffered term, "serial" (one transition at a time), "wy" (every slot's
+    coefficient at once from a triangular system, paper App. C.1) or "proj"
+    (the same coefficients, with C q~ formed from per-slot factors projected
+    through the coefficient map when each slot is appended, paper App. C.2;
+    self.rp holds them).
     """
 
     def __init__(self, family: str, dk: int, dv: int, W: int, ranks: np.ndarray,
@@ -153,6 +156,7 @@ class OracleLayer:
         ident = 0.0 if family == "mamba2" else 1.0
         self.rg = np.full((n, W, self.gl), ident)
         self.rb = None if family == "mamba2" else np.zeros((n, W))
+        self.rp = np.zeros((n, W, self.rmax))   # projected factors (pullback "proj")
         self.count = np.zeros(n, dtype=np.int32) if count0 is None else \
             np.ascontiguousarray(np.asarray(count0, dtype=np.int32).reshape(n)).copy()
         self.L = _Layer(FAMILY[family], dk, dv, W, self.rmax, STORE[state_store],
@@ -163,7 +167,7 @@ class OracleLayer:
     def _tiles_struct(self):
         return _Tiles(self.n, _p(self.rank, _IP), _p(self.S), _p(self.U), _p(self.Pt),
                       _p(self.C), _p(self.A), _p(self.rk), _p(self.rv), _p(self.rg),
-                      _p(self.rb), _p(self.count, _IP), _p(self.Sc))
+                      _p(self.rb), _p(self.count, _IP), _p(self.Sc), _p(self.rp))
 
     def gather_step(self, step, seq_rows: Optional[np.ndarray] = None):
         """Per-tile arrays from a layer-shaped StepInputs (rows = sequences).

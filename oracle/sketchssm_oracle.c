@@ -58,7 +58,7 @@ enum { ORC_MAMBA2 = 0, ORC_GDN = 1, ORC_KDA = 2 };
 enum { ORC_STORE_EXACT = 0, ORC_STORE_F32 = 1, ORC_STORE_BF16 = 2 };
 enum { ORC_OK = 0, ORC_ERR_COUNT = 1 };
 enum { ORC_COEF_FIXED = 0, ORC_COEF_STATE = 1 };
-enum { ORC_PULLBACK_SERIAL = 0, ORC_PULLBACK_WY = 1 };
+enum { ORC_PULLBACK_SERIAL = 0, ORC_PULLBACK_WY = 1, ORC_PULLBACK_PROJ = 2 };
 
 typedef struct {
     int family;
@@ -70,7 +70,8 @@ typedef struct {
     int coef_mode;     /* ORC_COEF_FIXED: C is an input table;
                           ORC_COEF_STATE: the flush writes C from the new state */
     double coef_ridge; /* ORC_COEF_STATE: ridge relative to the mean Gram eigenvalue */
-    int pullback;      /* the sketched read's effective query: ORC_PULLBACK_SERIAL or _WY */
+    int pullback;      /* the sketched read's effective query: ORC_PULLBACK_SERIAL, _WY, or
+                          _PROJ (the WY coefficients with projected per-slot factors) */
 } orc_layer;
 
 /* n independent tiles; every array is indexed by tile first. */
@@ -90,6 +91,9 @@ typedef struct {
     int* count;          /* [n] entries buffered since the last flush */
     double* Sc;          /* [n][dk][dv] state copy of dense-fallback tiles (rank 0), stored
                             in the sketch dtype; may be NULL when no tile has rank 0 */
+    double* rp;          /* [n][W][rmax] ORC_PULLBACK_PROJ: the ring's projected factors
+                            C (Gamma_s (.) k_s), stored at the state's precision; may be
+                            NULL otherwise */
 } orc_tiles;
 
 typedef struct {
@@ -217,6 +221,7 @@ static void state_read(const orc_layer* L, const double* S, const double* x, dou
 #define RV(T, L, i, s) ((T)->rv + ((size_t)(i) * (L)->W + (s)) * (L)->dv)
 #define RG(T, L, i, s) ((T)->rg + ((size_t)(i) * (L)->W + (s)) * gate_len(L))
 #define RB(T, L, i, s) ((T)->rb ? (T)->rb[(size_t)(i) * (L)->W + (s)] : 0.0)
+#define RP(T, L, i, s) ((T)->rp + ((size_t)(i) * (L)->W + (s)) * (L)->rmax)
 
 static double tile_A(const orc_tiles* T, int i) { return T->A ? T->A[i] : 0.0; }
 
@@ -271,7 +276,7 @@ static double slot_decay(const orc_layer* L, const orc_tiles* T, int i, int p, i
  *     q~    = D(-1,n-1) q - sum_l e beta_l d_l D(-1,l) k_l,
  *     o_buf = sum_l s_l d_l v_l   (s_l the slot's write scale). */
 static void effective_query_wy(const orc_layer* L, const orc_tiles* T, int i, int n,
-                               const double* q, double* r, double* obuf) {
+                               const double* q, double* r, double* obuf, double* dcoef) {
     const int dk = L->dk;
     const int erase = L->family != ORC_MAMBA2;
     double* Lm = (double*)calloc((size_t)(n > 0 ? n : 1) * (n > 0 ? n : 1), sizeof(double));
@@ -315,7 +320,61 @@ static void effective_query_wy(const orc_layer* L, const orc_tiles* T, int i, in
         const double* v = RV(T, L, i, l);
         for (int j = 0; j < L->dv; ++j) obuf[j] += w * v[j];
     }
+    if (dcoef)
+        for (int l = 0; l < n; ++l) dcoef[l] = d[l];
     free(Lm); free(b); free(d); free(D);
+}
+
+/* The product of the decays of slots 0..s at key element m: D(-1, s) in
+ * the notation above (Gamma_s). */
+static double gamma_to(const orc_layer* L, const orc_tiles* T, int i, int s, int m) {
+    double g = 1.0;
+    for (int p = 0; p <= s; ++p) g *= slot_decay(L, T, i, p, m);
+    return g;
+}
+
+/* Projected factor of ring slot s (paper App. C.2: the transition factors
+ * projected through the fixed coefficient map, so that a slot keeps an
+ * r-dimensional factor instead of a dk-dimensional one):
+ *     P_s = C (Gamma_s (.) k_s),
+ * with Gamma_s the product of the decays of slots 0..s (the decay part of
+ * D(-1, s) in the triangular system above; a scalar for GDN, per channel
+ * for KDA).  Formed when slot s is appended and stored at the state's
+ * precision. */
+static void project_slot(const orc_layer* L, orc_tiles* T, int i, int s) {
+    const int r = T->rank[i];
+    const double* k = RK(T, L, i, s);
+    const double* C = TC(T, L, i);
+    double* P = RP(T, L, i, s);
+    for (int j = 0; j < r; ++j) {
+        double t = 0.0;
+        for (int m = 0; m < L->dk; ++m) {
+            const double g = gamma_to(L, T, i, (g_mutation == 16 && s > 0) ? s - 1 : s, m);
+            t += C[(size_t)j * L->dk + m] * g * k[m];
+        }
+        P[j] = store(L->state_store, t);
+    }
+}
+
+/* c = C q~ from the projected factors (paper App. C.2): with the
+ * coefficients d_l of the triangular system,
+ *     q~ = Gamma_{n-1} (.) q - sum_l e beta_l d_l Gamma_l (.) k_l,
+ * so  C q~ = C (Gamma_{n-1} (.) q) - sum_l e beta_l d_l P_l,
+ * where only the first product touches a dk-dimensional vector. */
+static void coef_projected(const orc_layer* L, const orc_tiles* T, int i, int n, const double* q,
+                           const double* d, double* c) {
+    const int r = T->rank[i];
+    const int erase = L->family != ORC_MAMBA2;
+    const double* C = TC(T, L, i);
+    double* gq = (double*)malloc(sizeof(double) * L->dk);
+    for (int m = 0; m < L->dk; ++m) gq[m] = gamma_to(L, T, i, n - 1, m) * q[m];
+    for (int j = 0; j < r; ++j) {
+        double t = dot(C + (size_t)j * L->dk, gq, L->dk);
+        if (erase)
+            for (int l = 0; l < n; ++l) t -= RB(T, L, i, l) * d[l] * RP(T, L, i, l)[j];
+        c[j] = t;
+    }
+    free(gq);
 }
 
 /* Apply ring entries 0..n-1 in order to the fp64 copy S of the stored state. */
@@ -501,14 +560,24 @@ int orc_read(const orc_layer* L, orc_tiles* T, const orc_step* st) {
         double* c = (double*)malloc(sizeof(double) * (r > 0 ? r : 1));
         double* o = (double*)malloc(sizeof(double) * L->dv);
         const double* q = st->q + (size_t)i * L->dk;
-        if (L->pullback == ORC_PULLBACK_WY)
-            effective_query_wy(L, T, i, n, q, qt, obuf);
+        double* dco = NULL;
+        if (L->pullback == ORC_PULLBACK_PROJ) {
+            project_slot(L, T, i, n - 1);              /* the appended slot's factor */
+            dco = (double*)malloc(sizeof(double) * n);
+        }
+        if (L->pullback == ORC_PULLBACK_WY || L->pullback == ORC_PULLBACK_PROJ)
+            effective_query_wy(L, T, i, n, q, qt, obuf, dco);
         else
             effective_query(L, T, i, n, q, qt, obuf);
         const double* C = TC(T, L, i);
         const double* U = TU(T, L, i);
-        for (int j = 0; j < r; ++j)   /* c = C q~ */
-            c[j] = dot(C + (size_t)j * L->dk, g_mutation == 9 ? q : qt, L->dk);
+        if (dco) {                    /* c = C q~ from the projected factors */
+            coef_projected(L, T, i, n, q, dco, c);
+            free(dco);
+        } else {
+            for (int j = 0; j < r; ++j)   /* c = C q~ */
+                c[j] = dot(C + (size_t)j * L->dk, g_mutation == 9 ? q : qt, L->dk);
+        }
         if (r == 0)                   /* dense fallback: o = Sc^T q~ + o_buf */
             state_read(L, T->Sc + (size_t)i * L->dk * L->dv, g_mutation == 14 ? q : qt, o);
         for (int n2 = 0; n2 < L->dv; ++n2) {  /* o = U c + o_buf */
@@ -562,7 +631,7 @@ int orc_replay_step(const orc_layer* L, orc_tiles* T, const orc_step* st) {
     return err;
 }
 
-int orc_abi_version(void) { return 3; }
+int orc_abi_version(void) { return 4; }
 
 #ifdef _OPENMP
 #include <omp.h>

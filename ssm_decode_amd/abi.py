@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(HERE, "libsketchssm.so")
 # constants of include/sketchssm.h
 SKSSM_MAMBA2, SKSSM_GDN, SKSSM_KDA = 0, 1, 2
 SKSSM_F32, SKSSM_BF16 = 0, 1
-SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL = 0, 1
+SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL, SKSSM_FLUSH_DUE_SCAN = 0, 1, 2
 SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
-SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY = 0, 1
+SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY, SKSSM_PULLBACK_PROJ = 0, 1, 2
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5
 SKSSM_ESCRATCH = -6
 SKSSM_NOALLOC_SCRATCH_BYTES = 16777216
@@ -43,7 +43,7 @@ class sketchssm_buffers(C.Structure):
                 ("rank_offsets", C.c_void_p), ("ring_k", C.c_void_p), ("ring_v", C.c_void_p),
                 ("ring_gate", C.c_void_p), ("ring_beta", C.c_void_p), ("count", C.c_void_p),
                 ("A", C.c_void_p), ("err", C.c_void_p), ("work", C.c_void_p),
-                ("Cstate", C.c_void_p), ("Scopy", C.c_void_p)]
+                ("Cstate", C.c_void_p), ("Scopy", C.c_void_p), ("ring_pc", C.c_void_p)]
 
 
 class sketchssm_step(C.Structure):

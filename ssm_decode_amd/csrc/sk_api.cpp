@@ -43,7 +43,7 @@ bool any_dense(const sketchssm_layer* L) {
 // every head's basis, the key-query dot products and the checked ring fill.
 // GDN/KDA: only with dense-fallback heads, the pulled-back query and the
 // buffered term of each such tile, for the launch that reads the copies.
-int64_t workspace_bytes(const sketchssm_layer* L) {
+int64_t read_work_bytes(const sketchssm_layer* L) {
   if (L->family != SKSSM_MAMBA2) {
     int nd = 0;
     for (int h = 0; h < L->heads; ++h) nd += L->rank_offsets_host[h + 1] == L->rank_offsets_host[h];
@@ -53,6 +53,20 @@ int64_t workspace_bytes(const sketchssm_layer* L) {
   }
   const sk::M2Work w(L->batch, L->rank_offsets_host[L->heads], L->qk_groups, L->window);
   return (int64_t)w.total * 4;
+}
+
+// Workspace of a flush with SKSSM_FLUSH_DUE_SCAN: every region's count of
+// due tiles, then every region's list (sk_tile.hpp, DueWork).
+int64_t scan_work_bytes(const sketchssm_layer* L) {
+  if (L->batch == 0) return 0;
+  return (int64_t)sk::DueWork(L->batch, L->heads).total * 4;
+}
+
+// One workspace serves both: a call uses it only within itself, and calls on
+// one layer are ordered.
+int64_t workspace_bytes(const sketchssm_layer* L) {
+  const int64_t r = read_work_bytes(L), f = scan_work_bytes(L);
+  return r > f ? r : f;
 }
 
 int check_layer(const sketchssm_layer* L) {
@@ -70,7 +84,9 @@ int check_layer(const sketchssm_layer* L) {
   }
   if (!shape_supported(L->dk, L->dv)) return SKSSM_EDIM;
   if (L->coef_map != SKSSM_COEF_FIXED && L->coef_map != SKSSM_COEF_STATE) return SKSSM_EFLAG;
-  if (L->pullback != SKSSM_PULLBACK_SERIAL && L->pullback != SKSSM_PULLBACK_WY) return SKSSM_EFLAG;
+  if (L->pullback != SKSSM_PULLBACK_SERIAL && L->pullback != SKSSM_PULLBACK_WY &&
+      L->pullback != SKSSM_PULLBACK_PROJ)
+    return SKSSM_EFLAG;
   if (L->coef_map == SKSSM_COEF_STATE && !(isfinite(L->coef_ridge) && L->coef_ridge > 0.f))
     return SKSSM_EINVAL;
   if (L->window < 1 || L->window > kMaxW) return SKSSM_EDIM;
@@ -105,9 +121,13 @@ int check_buffers(const sketchssm_layer* L, const sketchssm_buffers* B, const sk
     if (!aligned16(B->ring_k) || !aligned16(B->ring_v) || !aligned16(B->ring_gate)) return SKSSM_EINVAL;
     if (L->family != SKSSM_MAMBA2 && !aligned16(B->ring_beta)) return SKSSM_EINVAL;
   }
+  // the projected factors: read and appended by the GDN/KDA read
+  if (nd.C && nd.ring && L->family != SKSSM_MAMBA2 && L->pullback == SKSSM_PULLBACK_PROJ &&
+      rows && !aligned16(B->ring_pc))
+    return SKSSM_EINVAL;
   if (nd.count && (!aligned16(B->count) || !aligned16(B->err))) return SKSSM_EINVAL;
   if (L->family == SKSSM_MAMBA2 && !aligned16(B->A)) return SKSSM_EINVAL;
-  if (nd.work && workspace_bytes(L) > 0 && !aligned16(B->work)) return SKSSM_EINVAL;
+  if (nd.work && read_work_bytes(L) > 0 && !aligned16(B->work)) return SKSSM_EINVAL;
   if (nd.step_in || nd.step_q || nd.step_o) {
     if (!S) return SKSSM_EINVAL;
     if (nd.step_in) {
@@ -150,6 +170,7 @@ sk::Params make_params(const sketchssm_layer* L, const sketchssm_buffers* B, con
   p.ndense = nd;
   p.ridge = L->coef_ridge;
   p.pullback = L->pullback;
+  p.rpc = B->ring_pc;
   if (S) {
     p.q = S->q;
     p.k = S->k;
@@ -197,7 +218,7 @@ int sketchssm_read_noalloc(const sketchssm_layer* layer, const sketchssm_buffers
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    const int64_t need = workspace_bytes(layer);
+    const int64_t need = read_work_bytes(layer);
     if (need > (int64_t)SKSSM_NOALLOC_SCRATCH_BYTES) return SKSSM_ESCRATCH;
     // (bufs->work is not used: the workspace is the library's scratch array)
     const Needs nd{false, true, false, true, true, true, true, true, true, false, true};
@@ -220,12 +241,19 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL) return SKSSM_EFLAG;
+    if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL && flags != SKSSM_FLUSH_DUE_SCAN)
+      return SKSSM_EFLAG;
     const bool out = step != nullptr;
     const Needs nd{true, true, true, false, true, true, false, out, out, false, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
+    const bool scan = flags == SKSSM_FLUSH_DUE_SCAN;
+    if (scan && layer->batch > 0 && !aligned16(bufs->work)) return SKSSM_EINVAL;
     sk::Params p = make_params(layer, bufs, step);
     p.flush_all = flags == SKSSM_FLUSH_ALL;
+    if (scan && layer->batch > 0) {
+      p.due_work = static_cast<int*>(bufs->work);
+      p.due_nreg = sk::due_regions(layer->batch, layer->heads);
+    }
     if (!out) {
       p.q = nullptr;
       p.o = nullptr;

@@ -334,6 +334,16 @@ __device__ __forceinline__ float low_lane_sum(float x) {
   return x;
 }
 
+// Between a wave's LDS stores and its loads of values other lanes of the
+// same wave stored: the wavefront-scope fences keep the compiler from moving
+// the loads above the stores (the lanes' accesses do not alias from one
+// lane's point of view), and the wave's LDS accesses then execute in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Value of lane L (a compile-time or wave-uniform index) in every lane.
 __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));

@@ -7,6 +7,34 @@
 
 namespace sk {
 
+// Compute units of the current device (cached: the figure only sizes a
+// grid, which is correct at any size).
+static int device_cus() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached = cus;
+  return cached;
+}
+
+// The flush over a device-side list of due tiles: the scan, then a grid of
+// eight workgroups per compute unit (about two rounds of resident
+// workgroups; a multiple of the region count), each taking every stride-th
+// listed tile of its region.
+template <void (*KERNEL)(Params)>
+static void launch_listed_flush(int threads, size_t lds, const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(due_scan_kernel<0>, dim3(p.due_nreg), dim3(64), 0, st, p);
+  const int cap = 8 * device_cus();
+  const int stride = (cap + p.due_nreg - 1) / p.due_nreg;
+  const int per_region = stride < DUE_RT ? stride : DUE_RT;
+  hipLaunchKernelGGL(KERNEL, dim3(p.due_nreg * per_region), dim3(threads), lds, st, p);
+}
+
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
 static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   const dim3 grid((p.seq_list ? p.nseq : p.B) * p.H), block(TileShape<DK, DV>::THREADS);
@@ -16,6 +44,18 @@ static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY, 0>::BYTES;
   // (the flush of a layer with dense-fallback heads is its own instantiation)
   const bool dense = p.ndense > 0;
+  if (mode == MODE_FLUSH && p.due_nreg > 0) {
+    constexpr int NT = TileShape<DK, DV>::THREADS;
+    if (coef && dense)
+      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true, true>>(NT, lds_flush_map, p, st);
+    else if (coef)
+      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false, true>>(NT, lds_flush_map, p, st);
+    else if (dense)
+      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true, true>>(NT, lds_flush, p, st);
+    else
+      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false, true>>(NT, lds_flush, p, st);
+    return 0;
+  }
   if (mode == MODE_FLUSH && coef && dense)
     hipLaunchKernelGGL((tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true>), grid, block, lds_flush_map, st, p);
   else if (mode == MODE_FLUSH && coef)
@@ -44,11 +84,14 @@ static void launch_read(const Params& p, hipStream_t st) {
       hipLaunchKernelGGL((m2_dense_read_kernel<DK, DV, AT, UT, WMAX>), dim3(p.B * p.ndense), dim3(64), 0,
                          st, p);
   } else {
-    if (p.pullback)
-      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, true>), dim3(dn_read_blocks(p.B, p.H)),
+    if (p.pullback == 2)
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, 2>), dim3(dn_read_blocks(p.B, p.H)),
+                         dim3(64 * DN_TPW), 0, st, p);
+    else if (p.pullback == 1)
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, 1>), dim3(dn_read_blocks(p.B, p.H)),
                          dim3(64 * DN_TPW), 0, st, p);
     else
-      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, false>), dim3(dn_read_blocks(p.B, p.H)),
+      hipLaunchKernelGGL((dn_read_kernel<FAM, DK, DV, AT, UT, WMAX, COEF, 0>), dim3(dn_read_blocks(p.B, p.H)),
                          dim3(64 * DN_TPW), 0, st, p);
     if (p.ndense > 0)
       hipLaunchKernelGGL((dn_dense_read_kernel<DK, DV, AT, UT>), dim3(p.B * p.ndense), dim3(DND_THREADS), 0,

@@ -18,6 +18,8 @@ struct Params {
   int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
   const int32_t* seq_list;  // MODE_FLUSH: device list of nseq sequences to flush, or null (all)
   int nseq;
+  int* due_work;        // MODE_FLUSH with a device-side due list: its part of the workspace
+  int due_nreg;         //   and the number of tile regions (0: no list)
   float* S;
   void* U;
   const float* Pt;
@@ -36,7 +38,9 @@ struct Params {
   int ndense;           // dense-fallback heads, in head order in dense_list; their state
   int16_t dense_list[DENSE_LIST_MAX];  // copies are Sc[b][position in the list]
   float ridge;          // relative ridge of the state-dependent map
-  int pullback;         // GDN/KDA read: 0 serial effective query, 1 the triangular-system form
+  int pullback;         // GDN/KDA read: 0 serial effective query, 1 the triangular-system form,
+                        // 2 that form with projected per-slot factors
+  float* rpc;           // pullback 2: the ring's projected factors [B][H][W][16] fp32
   const void* q;
   const void* k;
   const void* v;
@@ -70,6 +74,25 @@ struct DnWork {
     total = flag + ((size_t)B * D + 63) / 64 * 64;
   }
 };
+
+// Due tiles listed on the device for a flush (SKSSM_FLUSH_DUE_SCAN): the
+// tiles (b * H + h) are split into regions of DUE_RT consecutive tiles; a
+// region's due tiles are listed in its own slice of the workspace, after
+// every region's number of them (int32 offsets).
+constexpr int DUE_RT = 1024;       // tiles per region: 16 per lane of one wave
+
+struct DueWork {
+  size_t cnt, list, total;
+  __host__ __device__ DueWork(int B, int H) {
+    const size_t nreg = ((size_t)B * H + DUE_RT - 1) / DUE_RT;
+    cnt = 0;
+    list = (nreg + 63) / 64 * 64;
+    total = list + nreg * DUE_RT;
+  }
+};
+__host__ __device__ inline int due_regions(int B, int H) {
+  return (int)(((size_t)B * H + DUE_RT - 1) / DUE_RT);
+}
 
 // Position of dense-fallback head h in the list (h must be listed).
 __host__ __device__ inline int dense_slot(const Params& p, int h) {

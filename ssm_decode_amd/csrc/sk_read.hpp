@@ -355,6 +355,7 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
       }
     }
     ch[s] = cqv;
+    wave_lds_sync();                             // the row's lanes read eh and ch below
 
     // ------------------------------------------------------- output
     float acc[CPL], ob[CPL];
@@ -521,7 +522,10 @@ constexpr int DN_TPW = 4;            // tiles (waves) per workgroup
 
 __host__ __device__ inline int dn_read_blocks(int B, int H) { return (B + DN_TPW - 1) / DN_TPW * H; }
 
-template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF, bool WY>
+// PB: the effective query and buffered term of a read: 0 serial, 1 every
+// slot's coefficient from the triangular system (WY form), 2 the same
+// coefficients with C q~ formed from per-slot projected factors.
+template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX, int COEF, int PB>
 __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   constexpr int EK = DK >= 64 ? DK / 64 : 1;
   constexpr int EV = DV >= 64 ? DV / 64 : 1;
@@ -532,6 +536,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   __shared__ __align__(16) float s_c[COEF ? 1 : 16 * DK];
   // the triangular system of the parallel pull-back, per wave: L [WMAX][WMAX], then d [WMAX]
   constexpr int WYS = WMAX * WMAX + WMAX;
+  constexpr bool WY = PB != 0;
   __shared__ __align__(16) float s_wy[WY ? DN_TPW * WYS : 1];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -610,6 +615,15 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
       if (FAM == FAM_KDA) ldn<KG>(ring_g + (size_t)i * DK, gs[i]);
     }
   }
+  // projected factors (PB = 2): lane j of every row of 16 holds factor
+  // element j of each buffered slot
+  float pcs[PB == 2 ? WMAX - 1 : 1];
+  if constexpr (PB == 2) {
+    const float* pc = p.rpc + bh * W * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < WMAX - 1; ++i)
+      if (i < nr && rk > 0) pcs[i] = pc[(size_t)i * 16];
+  }
   // GDN / KDA per-slot scalars: slot i in lane i
   const int ls = lane < nr ? lane : 0;
   const float al_l = FAM == FAM_GDN ? ring_g[ls] : 1.f;
@@ -649,6 +663,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
     return;
   }
 
+  float pcur = 0.f;                              // PB = 2: lane j's element of the step's factor
   if (rd) {
     // ---------------------------------------- pull-back, newest first
     float ob[EV];
@@ -730,6 +745,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
           if (lane == 0) dw[j] = bj;
         }
       }
+      wave_lds_sync();                           // lane 0's table entries, read by every lane
       // back substitution: lane l holds d_l once it is known and reads row j
       // of the table at column l, so each d_j is one wave sum (the table
       // reads do not wait for the solution; a wave's LDS accesses complete
@@ -744,6 +760,9 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
           dlane = lane == j ? dj : dlane;
         }
       }
+      // (with projected factors a sketched head needs only D(-1, n0) here:
+      // the erase terms enter its coefficients through the factors)
+      const bool qt_terms = PB != 2 || rk == 0;   // uniform
       float D[EK], acc[EK];
 #pragma unroll
       for (int e = 0; e < EK; ++e) { D[e] = 1.f; acc[e] = 0.f; }
@@ -752,12 +771,57 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
         if (l <= n0) {
           decay(l, D);                             // D = D(-1, l)
           const float bd = beta_of(l) * lane_value(dlane, l);
-          const VecN<AT, EK> kv = key(l);
           const VecN<AT, EV> vv = l < n0 ? vs[l < WMAX - 1 ? l : 0] : vcur;
+          if (qt_terms) {
+            const VecN<AT, EK> kv = key(l);
 #pragma unroll
-          for (int e = 0; e < EK; ++e) acc[e] -= bd * D[e] * vget(kv, e);
+            for (int e = 0; e < EK; ++e) acc[e] -= bd * D[e] * vget(kv, e);
+          }
 #pragma unroll
           for (int e = 0; e < EV; ++e) ob[e] += bd * vget(vv, e);
+        }
+      }
+      if constexpr (PB == 2) {
+        if (!qt_terms) {
+          // C q~ = C (D(-1,n0) q) - sum_l beta_l d_l P_l (paper App. C.2),
+          // with P_l = C (D(-1,l) k_l) stored when slot l was appended; the
+          // step's own factor P_n0 = C (D(-1,n0) k_n0) is formed here and
+          // appended.  pc_acc (lane j): sum over the buffered slots of
+          // beta_l d_l P_l[j].
+          float pc_acc = 0.f;
+#pragma unroll
+          for (int l = 0; l < WMAX - 1; ++l)
+            if (l < n0) pc_acc += lane_value(be_l, l) * lane_value(dlane, l) * pcs[l];
+          const float wcur = bcur * lane_value(dlane, n0);
+          float cq[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (j < rk) {                              // uniform
+              float cj[EK];
+              if constexpr (COEF) {
+#pragma unroll
+                for (int e = 0; e < EK; ++e) cj[e] = cr[j][e];
+              } else {
+                ldn<EK>(s_c + j * DK + lk, cj);
+              }
+              float aq = 0.f, ak = 0.f;
+#pragma unroll
+              for (int e = 0; e < EK; ++e) {
+                aq += cj[e] * D[e] * r[e];
+                ak += cj[e] * D[e] * vget(kcur, e);
+              }
+              const float pj = wave_sum(kl ? ak : 0.f);       // P_n0[j]
+              pcur = lane == j ? pj : pcur;
+              cq[j] = wave_sum(kl ? aq : 0.f) - lane_value(pc_acc, j) - wcur * pj;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (j < rk) {
+              const float c = cq[j];
+#pragma unroll
+              for (int e = 0; e < EV; ++e) ob[e] += c * vget(us[j], e);
+            }
         }
       }
 #pragma unroll
@@ -765,13 +829,14 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
     }
 
     // -------------------------- c = C_h r, then o = U_h c + o_buf
-    // (each c_j is a wave sum, wave-uniform, so U_h c needs no broadcast)
+    // (each c_j is a wave sum, wave-uniform, so U_h c needs no broadcast;
+    // with projected factors U_h c is already in ob)
     float out[EV];
 #pragma unroll
     for (int e = 0; e < EV; ++e) out[e] = ob[e];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      if (j < rk) {                                // uniform
+      if (j < rk && PB != 2) {                     // uniform
         float cj[EK];
         if constexpr (COEF) {
 #pragma unroll
@@ -809,6 +874,7 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
   } else if (lane == 0) {
     ring_g[n0] = gcur[0];
   }
+  if (PB == 2 && rd && lane < rk) p.rpc[(bh * W + n0) * 16 + lane] = pcur;
   if (lane == 0) {
     ring_b[n0] = bcur;
     p.count[bh] = n;

@@ -41,7 +41,8 @@ class DeviceStep:
 
 
 COEF = {"fixed": abi.SKSSM_COEF_FIXED, "state": abi.SKSSM_COEF_STATE}
-PULLBACK = {"serial": abi.SKSSM_PULLBACK_SERIAL, "wy": abi.SKSSM_PULLBACK_WY}
+PULLBACK = {"serial": abi.SKSSM_PULLBACK_SERIAL, "wy": abi.SKSSM_PULLBACK_WY,
+            "proj": abi.SKSSM_PULLBACK_PROJ}
 
 
 class DecodeLayer:
@@ -50,8 +51,9 @@ class DecodeLayer:
     the read's workspace.  coef = "fixed" reads the per-head map Cmap;
     coef = "state" has every flush write each tile's own map into Cstate
     ([B][R][dk], sketch dtype) with the relative ridge ``ridge``.
-    pullback = "serial" or "wy" selects how a GDN/KDA read evaluates the
-    effective query and the buffered term (Mamba-2 ignores it)."""
+    pullback = "serial", "wy" or "proj" selects how a GDN/KDA read evaluates
+    the effective query and the buffered term (Mamba-2 ignores it); "proj"
+    keeps the ring's projected factors in ring_pc."""
 
     def __init__(self, family: str, batch: int, heads: int, qk_groups: int, dk: int, dv: int,
                  window: int, act: str, sketch: str, rank_offsets: np.ndarray,
@@ -92,6 +94,8 @@ class DecodeLayer:
             self.ring_gate = torch.ones((B, H, W, dk), dtype=torch.float32, device=device)
             self.ring_beta = z((B, H, W), torch.float32)
             self.A = None
+        # projected per-slot factors of the "proj" pull-back (GDN/KDA)
+        self.ring_pc = z((B, H, W, 16), torch.float32) if (pullback == "proj" and family != "mamba2") else None
         self.count = z((B, H), torch.int32)
         self.err = z((4,), torch.int32)
         self._layer = abi.sketchssm_layer(
@@ -106,7 +110,7 @@ class DecodeLayer:
             _ptr(self.S), _ptr(self.U), _ptr(self.Pt), _ptr(self.Cmap), _ptr(self.offsets),
             _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_gate), _ptr(self.ring_beta),
             _ptr(self.count), _ptr(self.A), _ptr(self.err), _ptr(self.work), _ptr(self.Cstate),
-            _ptr(self.Scopy))
+            _ptr(self.Scopy), _ptr(self.ring_pc))
 
     # -------------------------------------------------------------- structs
     @property

@@ -98,7 +98,9 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     the effective query of a GDN/KDA read from the triangular system over
     the buffered slots.  flush = "list": the sketch path flushes through
     sketchssm_flush_seqs with each step's due sequences (from the window
-    phases) instead of the due-flag flush.
+    phases) instead of the due-flag flush; flush = "scan": through
+    sketchssm_flush with SKSSM_FLUSH_DUE_SCAN (the due tiles listed on the
+    device).
 
     Gates: the relative L2 error pooled over the compared tiles, and the same
     error of every tile on its own (o per step; S, U and C per flush).
@@ -174,6 +176,8 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
             assert lay.read(step) == 0
             if flush == "list":
                 assert lay.flush_seqs(step, due_list(t)) == 0
+            elif flush == "scan":
+                assert lay.flush(step, abi.SKSSM_FLUSH_DUE_SCAN) == 0
             else:
                 assert lay.flush(step, abi.SKSSM_FLUSH_DUE) == 0
             rc, _ = orc.read(si, seq_rows=seq_rows, o=o_ref)

@@ -57,7 +57,7 @@ def _layer(offsets, family=abi.SKSSM_MAMBA2, batch=2, heads=4, groups=4, dk=16, 
 def _bufs(**over):
     f = dict(S=FAKE, U=FAKE, Pt=FAKE, C=FAKE, rank_offsets=FAKE, ring_k=FAKE, ring_v=FAKE,
              ring_gate=FAKE, ring_beta=FAKE, count=FAKE, A=FAKE, err=FAKE, work=FAKE, Cstate=FAKE,
-             Scopy=FAKE)
+             Scopy=FAKE, ring_pc=FAKE)
     f.update(over)
     return abi.sketchssm_buffers(**f)
 
@@ -137,8 +137,19 @@ def test_null_and_misaligned_pointers(lib):
 
 
 def test_bad_flag(lib):
-    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 2) == abi.SKSSM_EFLAG
+    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 3) == abi.SKSSM_EFLAG
     assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, -1) == abi.SKSSM_EFLAG
+
+
+def test_scan_flush_needs_the_workspace(lib):
+    """SKSSM_FLUSH_DUE_SCAN lists the due tiles in bufs.work: a missing or
+    misaligned workspace is EINVAL; batch 0 is a no-op."""
+    for fam in (abi.SKSSM_MAMBA2, abi.SKSSM_GDN, abi.SKSSM_KDA):
+        L = _layer(OK_OFF, family=fam)
+        assert abi.sketchssm_flush(L, _bufs(work=None), None, abi.SKSSM_FLUSH_DUE_SCAN) == abi.SKSSM_EINVAL
+        assert abi.sketchssm_flush(L, _bufs(work=FAKE + 8), None, abi.SKSSM_FLUSH_DUE_SCAN) == abi.SKSSM_EINVAL
+        L0 = _layer(OK_OFF, family=fam, batch=0)
+        assert abi.sketchssm_flush(L0, _bufs(work=None), None, abi.SKSSM_FLUSH_DUE_SCAN) == 0
 
 
 def _m2_work_bytes(B, R, G, W):
@@ -149,13 +160,27 @@ def _m2_work_bytes(B, R, G, W):
     return 4 * (a64(B * R) + a64(B * G * W) + a64(B * G))
 
 
+def _scan_work_bytes(B, H):
+    # the scan flush's due list: per region of 1024 tiles its count (the
+    # counts rounded up to 64 entries), then its 1024-entry list, int32
+    nreg = (B * H + 1023) // 1024
+    return 4 * ((nreg + 63) // 64 * 64 + nreg * 1024)
+
+
 def test_workspace_bytes(lib):
-    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == _m2_work_bytes(2, 16, 4, 4) == 768
+    """The workspace is the larger of the read's and the scan flush's needs."""
+    assert _m2_work_bytes(2, 16, 4, 4) == 768 and _scan_work_bytes(2, 4) == 4352
+    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 4352
     off = np.concatenate([[0], np.cumsum(np.full(128, 8))]).astype(np.int32)
     L = _layer(off, batch=320, heads=128, groups=8, dk=128, dv=64, W=16)
+    assert _m2_work_bytes(320, 1024, 8, 16) > _scan_work_bytes(320, 128)
     assert abi.sketchssm_workspace_bytes(L) == _m2_work_bytes(320, 1024, 8, 16)
+    L = _layer(off, batch=1024, heads=128, groups=8, dk=128, dv=64, W=32)
+    assert abi.sketchssm_workspace_bytes(L) == max(_m2_work_bytes(1024, 1024, 8, 32),
+                                                   _scan_work_bytes(1024, 128))
     for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
-        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == 0
+        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == _scan_work_bytes(2, 4)
+        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam, batch=0)) == 0
     assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, W=0)) == abi.SKSSM_EDIM
     assert abi.sketchssm_workspace_bytes(None) == abi.SKSSM_EINVAL
 
@@ -173,12 +198,14 @@ def test_workspace_bytes_delta_rule_dense_heads(lib):
     heads, and then the read requires it."""
     for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
         L = _layer([0, 4, 4, 8, 8], family=fam, batch=3)          # heads 1 and 3 dense
-        assert abi.sketchssm_workspace_bytes(L) == _dn_work_bytes(3, 2, 16, 32) == 1536
+        assert _dn_work_bytes(3, 2, 16, 32) == 1536
+        assert abi.sketchssm_workspace_bytes(L) == max(1536, _scan_work_bytes(3, 4))
         assert abi.sketchssm_read(L, _bufs(work=None), _step()) == abi.SKSSM_EINVAL
         assert abi.sketchssm_read(L, _bufs(work=FAKE + 4), _step()) == abi.SKSSM_EINVAL
         off = np.concatenate([[0], np.cumsum([0] + [8] * 31)]).astype(np.int32)
         L = _layer(off, family=fam, batch=256, heads=32, groups=32, dk=128, dv=128, W=16)
-        assert abi.sketchssm_workspace_bytes(L) == _dn_work_bytes(256, 1, 128, 128)
+        assert abi.sketchssm_workspace_bytes(L) == max(_dn_work_bytes(256, 1, 128, 128),
+                                                       _scan_work_bytes(256, 32))
 
 
 def test_read_needs_its_workspace(lib):
@@ -217,16 +244,27 @@ def test_coefficient_map_mode(lib):
 
 
 def test_pullback_mode(lib):
-    """The pull-back mode is a flag: serial or the triangular-system form;
-    unknown values are EFLAG on every call."""
-    for bad in (2, -1):
+    """The pull-back mode is a flag: serial, the triangular-system form or
+    that form with projected factors; unknown values are EFLAG on every
+    call.  The projected form's GDN/KDA read needs the factor ring."""
+    for bad in (3, -1):
         L = _layer(OK_OFF, family=abi.SKSSM_GDN)
         L.pullback = bad
         assert _all_calls(L, _bufs(), _step()) == [abi.SKSSM_EFLAG] * 4
     for fam in (abi.SKSSM_MAMBA2, abi.SKSSM_GDN, abi.SKSSM_KDA):
-        L = _layer(OK_OFF, family=fam, batch=0)
-        L.pullback = abi.SKSSM_PULLBACK_WY
-        assert _all_calls(L, _bufs(), _step()) == [0] * 4
+        for pb in (abi.SKSSM_PULLBACK_WY, abi.SKSSM_PULLBACK_PROJ):
+            L = _layer(OK_OFF, family=fam, batch=0)
+            L.pullback = pb
+            assert _all_calls(L, _bufs(), _step()) == [0] * 4
+    for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
+        L = _layer(OK_OFF, family=fam)
+        L.pullback = abi.SKSSM_PULLBACK_PROJ
+        for bad in (None, FAKE + 4):
+            assert abi.sketchssm_read(L, _bufs(ring_pc=bad), _step()) == abi.SKSSM_EINVAL
+            assert abi.sketchssm_read_noalloc(L, _bufs(ring_pc=bad), _step()) == abi.SKSSM_EINVAL
+        # the flush and the baselines do not read the factors
+        assert abi.sketchssm_flush(_layer(OK_OFF, family=fam, batch=0), _bufs(ring_pc=None), None,
+                                   abi.SKSSM_FLUSH_ALL) == 0
 
 
 def test_dense_fallback_heads(lib):
@@ -242,7 +280,8 @@ def test_dense_fallback_heads(lib):
     assert abi.sketchssm_full_step(_layer([0, 4, 4, 8, 12]), _bufs(Scopy=None), None) == abi.SKSSM_EINVAL
     Ld = _layer([0, 0, 0, 0, 0], batch=0)            # every head dense: R = 0
     assert _all_calls(Ld, _bufs(U=None, Pt=None, C=None, Cstate=None), _step()) == [0] * 4
-    assert abi.sketchssm_workspace_bytes(_layer([0, 0, 0, 0, 0])) == _m2_work_bytes(2, 0, 4, 4)
+    assert abi.sketchssm_workspace_bytes(_layer([0, 0, 0, 0, 0])) == max(_m2_work_bytes(2, 0, 4, 4),
+                                                                      _scan_work_bytes(2, 4))
     # at most 64 dense heads per layer
     off = np.concatenate([[0], np.cumsum([0] * 65 + [4] * 63)]).astype(np.int32)
     assert abi.sketchssm_read(_layer(off, heads=128, groups=128, family=abi.SKSSM_GDN, batch=0),

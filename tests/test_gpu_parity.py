@@ -163,6 +163,32 @@ def test_flush_list_stress_w32():
     run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False, flush="list")
 
 
+# ------------- the flush over a device-side list of due tiles vs oracle
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
+def test_flush_scan_small_batch(name):
+    cfg = CONFIGS[name].with_(name=name + "_scan", batch=5, ragged=True, steps=40)
+    run(cfg, "sketch", flush="scan")
+
+
+@pytest.mark.parametrize("W,G", [(32, 8), (8, 16)])
+def test_flush_scan_stress(W, G):
+    """Batch 1024, ragged, flushed through SKSSM_FLUSH_DUE_SCAN for the full
+    512 steps on sampled tiles."""
+    from tests.gpu_parity import sample_tiles
+    cfg = [c for c in sweep_configs() if (c.window, c.mean_rank) == (W, G)][0]
+    tiles = sample_tiles(cfg, 4, 3, seed=cfg.seed + 2)
+    run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False, flush="scan")
+
+
+def test_flush_scan_aligned_full_batch():
+    """The aligned batch-320 layer (every tile due at once: the listed flush's
+    workgroups each take many tiles) on sampled tiles, three windows."""
+    from tests.gpu_parity import sample_tiles
+    cfg = CONFIGS["m2_b320"]
+    run(cfg, "sketch", steps=3 * cfg.window, tiles=sample_tiles(cfg, 4, 4, seed=cfg.seed + 1),
+        numpy_all=False, flush="scan")
+
+
 # ------------- the delta rule's 32-slot chunked flush at the real head shape
 @pytest.mark.parametrize("flush", ["due", "list"])
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])

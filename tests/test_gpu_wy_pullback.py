@@ -1,5 +1,6 @@
-"""The parallel (triangular-system) pull-back of the GDN/KDA read on the GPU
-against the oracle's own parallel form (needs a GPU).  Outputs, states and
+"""The parallel (triangular-system) pull-back of the GDN/KDA read on the GPU,
+and the same with projected per-slot factors (paper App. C.2), against the
+oracle's own forms (needs a GPU).  Outputs, states and
 sketches at the usual tolerances, over several windows, in the layouts the
 serial form is tested in: small ragged layers, both window capacities,
 64x64 heads, tiny gates, the state-dependent map, dense-fallback heads and
@@ -21,11 +22,14 @@ def _lib():
     abi.load()
 
 
-def run(cfg, **kw):
+PB = pytest.mark.parametrize("pb", ["wy", "proj"])
+
+
+def run(cfg, pb, **kw):
     from tests.gpu_parity import run_parity
-    print(f"\n[wy pull-back] {cfg.name} B={cfg.batch} H={cfg.heads} W={cfg.window} "
+    print(f"\n[{pb} pull-back] {cfg.name} B={cfg.batch} H={cfg.heads} W={cfg.window} "
           f"ragged={cfg.ragged} {kw.get('coef', 'fixed')}", flush=True)
-    return run_parity(cfg, "sketch", pullback="wy", **kw)
+    return run_parity(cfg, "sketch", pullback=pb, **kw)
 
 
 def _tiny(family, seed, **kw):
@@ -37,37 +41,43 @@ def _tiny(family, seed, **kw):
 
 
 @pytest.mark.parametrize("family,seed", [("gdn", 61), ("kda", 62)])
-def test_tiny(family, seed):
-    run(_tiny(family, seed))
+@PB
+def test_tiny(family, seed, pb):
+    run(_tiny(family, seed), pb)
 
 
 @pytest.mark.parametrize("family,W", [("gdn", 1), ("kda", 2), ("gdn", 16), ("kda", 32)])
-def test_window_sizes(family, W):
-    run(_tiny(family, 63 + W, window=W, steps=2 * W + 5, name=f"tiny_wy_{family}_W{W}"))
+@PB
+def test_window_sizes(family, W, pb):
+    run(_tiny(family, 63 + W, window=W, steps=2 * W + 5, name=f"tiny_wy_{family}_W{W}"), pb)
 
 
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
-def test_small_batch_ragged(name):
-    run(CONFIGS[name].with_(name=name + "_wy", batch=3, ragged=True, steps=36))
+@PB
+def test_small_batch_ragged(name, pb):
+    run(CONFIGS[name].with_(name=name + "_wy", batch=3, ragged=True, steps=36), pb)
 
 
 @pytest.mark.parametrize("family", ["gdn", "kda"])
-def test_head_64x64(family):
+@PB
+def test_head_64x64(family, pb):
     run(CONFIGS[family + "_b256"].with_(name=f"{family}_64x64_wy", dk=64, dv=64, batch=2, steps=20,
-                                         ragged=True))
+                                         ragged=True), pb)
 
 
-def test_state_map_and_dense_heads():
+@PB
+def test_state_map_and_dense_heads(pb):
     run(CONFIGS["kda_b256"].with_(name="kda_wy_map_dense", batch=2, ragged=True, steps=24,
-                                  dense_heads=(3,)), coef="state")
+                                  dense_heads=(3,)), pb, coef="state")
     run(CONFIGS["gdn_b256"].with_(name="gdn_wy_dense", batch=2, ragged=True, steps=24,
-                                  dense_heads=(0, 7)))
+                                  dense_heads=(0, 7)), pb)
 
 
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
-def test_full_batch_sampled(name):
+@PB
+def test_full_batch_sampled(name, pb):
     """Full batch in the benchmark's launch configuration, the oracle
     following sampled tiles."""
     from tests.gpu_parity import sample_tiles
     cfg = CONFIGS[name]
-    run(cfg, steps=2 * cfg.window + 6, tiles=sample_tiles(cfg, 3, 3, seed=cfg.seed), numpy_all=False)
+    run(cfg, pb, steps=2 * cfg.window + 6, tiles=sample_tiles(cfg, 3, 3, seed=cfg.seed), numpy_all=False)
