@@ -472,7 +472,8 @@ TRAFFIC = {
     "kda_b256": {"bytes": 1213516995,
                  "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
 }
-FLUSH_SOURCES = ("sk_tile.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp")
+FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
+                 "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
 
 
 def flush_src_digest():

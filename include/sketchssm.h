@@ -95,9 +95,9 @@ extern "C" {
 /* flush flags */
 #define SKSSM_FLUSH_DUE 0 /* flush tiles whose ring holds W entries */
 #define SKSSM_FLUSH_ALL 1 /* flush every tile (prime U, or retire sequences) */
-#define SKSSM_FLUSH_DUE_SCAN 2 /* as SKSSM_FLUSH_DUE, with the due tiles first listed on
-                                  the device (in bufs->work), so that a ragged window phase
-                                  launches workgroups for the due tiles only */
+#define SKSSM_FLUSH_DUE_SCAN 2 /* as SKSSM_FLUSH_DUE, with the due sequences first listed
+                                  on the device (in bufs->work), so that a ragged window
+                                  phase launches workgroups for the due tiles only */
 
 /* return codes */
 #define SKSSM_OK 0
@@ -211,13 +211,20 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * C = (G + lambda I)^{-1} Y, lambda = coef_ridge * trace(G) / r_h, stored in
  * the sketch dtype (C = 0 when the sketch is zero).
  * SKSSM_FLUSH_DUE_SCAN (paper App. B: each sequence flushes when its own
- * window fills): the same result as SKSSM_FLUSH_DUE, for callers that do not
- * track window phases.  A first launch lists the tiles whose count is W in
- * bufs->work (sketchssm_workspace_bytes; 16-byte aligned) and reports counts
- * outside [0, W] (SKSSM_ERRBIT_COUNT, tile untouched); the flush then runs a
- * grid of about one round of resident workgroups over the listed tiles, so
- * that a ragged phase (about batch / W sequences due a step) does not pay a
- * workgroup per tile of the batch. */
+ * window fills): the same result as SKSSM_FLUSH_DUE for callers that do not
+ * track window phases, given that every head of a sequence holds the same
+ * count (sketchssm_read appends, and the flushes reset, all heads of a
+ * sequence together).  A first launch (one workgroup) lists, in sequence
+ * order, the sequences whose head-0 count is W in bufs->work
+ * (sketchssm_workspace_bytes; 16-byte aligned) and reports head-0 counts
+ * outside [0, W] (SKSSM_ERRBIT_COUNT).  The flush then runs a workgroup per
+ * tile of the first min(batch, 2 * ceil(batch / W) + 8) listed sequences
+ * (about twice what a ragged phase brings due at a step), each tile claimed
+ * as in sketchssm_flush_seqs, and a loop over the tiles of any further
+ * listed sequences in a grid of two workgroups per compute unit, so that a
+ * ragged phase does not pay a workgroup per tile of the batch and an
+ * aligned one still flushes every tile.  The counts of the other heads are
+ * checked in listed sequences only. */
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,
                     void* hip_stream);
@@ -266,8 +273,8 @@ int sketchssm_replay_step(const sketchssm_layer* layer, const sketchssm_buffers*
  * heads: per (sequence, dense head) the pulled-back query (dk fp32), the
  * buffered term (dv fp32) and a flag (int32), passed from the read's main
  * launch to the launch that reads the state copies.  The scan flush lists
- * the due tiles: per region of 1024 tiles (b * H + h) its number of due
- * tiles, then its list (int32).  The caller allocates it; the library never
+ * the due sequences: their number (int32 at byte 0), then from byte 256
+ * their indices (batch int32, rounded up to 64).  The caller allocates it; the library never
  * does. */
 int64_t sketchssm_workspace_bytes(const sketchssm_layer* layer);
 

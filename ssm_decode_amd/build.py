@@ -18,7 +18,8 @@ ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
-SOURCES = ["sk_api.cpp", "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip", "sk_noalloc.hip"]
+SOURCES = ["sk_api.cpp", "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip", "sk_m2_f32.hip", "sk_gdn_f32.hip",
+           "sk_kda_f32.hip", "sk_noalloc.hip"]
 
 
 def _compile(src: str, extra=(), tag: str = "") -> str:
@@ -38,12 +39,12 @@ def _stale(src: str, tag: str) -> bool:
     if not os.path.exists(obj):
         return True
     deps = [os.path.join(CSRC, src), os.path.join(ROOT, "include", "sketchssm.h")]
-    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".inc"))]
     t = os.path.getmtime(obj)
     return any(os.path.getmtime(d) > t for d in deps)
 
 
-def build(jobs: int = 4, extra=(), out: str = LIB, incremental: bool = False) -> str:
+def build(jobs: int = 8, extra=(), out: str = LIB, incremental: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library.
     extra: additional compiler flags (e.g. -D tuning macros); out: library path;
     incremental: recompile only the objects older than their sources."""

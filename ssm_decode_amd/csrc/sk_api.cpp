@@ -55,11 +55,11 @@ int64_t read_work_bytes(const sketchssm_layer* L) {
   return (int64_t)w.total * 4;
 }
 
-// Workspace of a flush with SKSSM_FLUSH_DUE_SCAN: every region's count of
-// due tiles, then every region's list (sk_tile.hpp, DueWork).
+// Workspace of a flush with SKSSM_FLUSH_DUE_SCAN: the number of due
+// sequences, then their list (sk_params.hpp, DueWork).
 int64_t scan_work_bytes(const sketchssm_layer* L) {
   if (L->batch == 0) return 0;
-  return (int64_t)sk::DueWork(L->batch, L->heads).total * 4;
+  return (int64_t)sk::DueWork(L->batch).total * 4;
 }
 
 // One workspace serves both: a call uses it only within itself, and calls on
@@ -252,7 +252,9 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
     p.flush_all = flags == SKSSM_FLUSH_ALL;
     if (scan && layer->batch > 0) {
       p.due_work = static_cast<int*>(bufs->work);
-      p.due_nreg = sk::due_regions(layer->batch, layer->heads);
+      p.seq_count = p.due_work + sk::DueWork(layer->batch).cnt;
+      p.seq_list = p.due_work + sk::DueWork(layer->batch).list;
+      p.nseq = sk::due_slots(layer->batch, layer->window);
     }
     if (!out) {
       p.q = nullptr;

@@ -22,17 +22,16 @@ static int device_cus() {
   return cached;
 }
 
-// The flush over a device-side list of due tiles: the scan, then a grid of
-// eight workgroups per compute unit (about two rounds of resident
-// workgroups; a multiple of the region count), each taking every stride-th
-// listed tile of its region.
-template <void (*KERNEL)(Params)>
-static void launch_listed_flush(int threads, size_t lds, const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(due_scan_kernel<0>, dim3(p.due_nreg), dim3(64), 0, st, p);
-  const int cap = 8 * device_cus();
-  const int stride = (cap + p.due_nreg - 1) / p.due_nreg;
-  const int per_region = stride < DUE_RT ? stride : DUE_RT;
-  hipLaunchKernelGGL(KERNEL, dim3(p.due_nreg * per_region), dim3(threads), lds, st, p);
+// The flush over a device-side list of due sequences: the scan; the
+// one-tile-per-workgroup flush of listed sequences over the first p.nseq
+// list entries (its workgroups past the list's length exit at once); then
+// a looping launch of two workgroups per compute unit for the entries past
+// p.nseq (under a ragged phase usually none: its workgroups exit at once).
+template <void (*ONE)(Params), void (*LOOP)(Params)>
+static void launch_scanned_flush(int threads, size_t lds, const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(due_scan_kernel<0>, dim3(1), dim3(DUE_SCAN_THREADS), 0, st, p);
+  hipLaunchKernelGGL(ONE, dim3(p.nseq * p.H), dim3(threads), lds, st, p);
+  hipLaunchKernelGGL(LOOP, dim3(2 * device_cus()), dim3(threads), lds, st, p);
 }
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
@@ -44,16 +43,20 @@ static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   constexpr size_t lds_replay = TileLds<FAM, DK, DV, WMAX, MODE_REPLAY, 0>::BYTES;
   // (the flush of a layer with dense-fallback heads is its own instantiation)
   const bool dense = p.ndense > 0;
-  if (mode == MODE_FLUSH && p.due_nreg > 0) {
+  if (mode == MODE_FLUSH && p.seq_count) {
     constexpr int NT = TileShape<DK, DV>::THREADS;
     if (coef && dense)
-      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true, true>>(NT, lds_flush_map, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true>,
+                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true, true>>(NT, lds_flush_map, p, st);
     else if (coef)
-      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false, true>>(NT, lds_flush_map, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false>,
+                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false, true>>(NT, lds_flush_map, p, st);
     else if (dense)
-      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true, true>>(NT, lds_flush, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true>,
+                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true, true>>(NT, lds_flush, p, st);
     else
-      launch_listed_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false, true>>(NT, lds_flush, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false>,
+                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false, true>>(NT, lds_flush, p, st);
     return 0;
   }
   if (mode == MODE_FLUSH && coef && dense)
@@ -127,12 +130,5 @@ static int launch_dtype(int mode, int coef, int dk, int dv, const Params& p, hip
   return -2;
 }
 
-template <int FAM>
-static int launch_family(int mode, int coef, int dk, int dv, int act, int sketch, const Params& p,
-                         hipStream_t st) {
-  if (act == DT_F32 && sketch == DT_F32) return launch_dtype<FAM, float, float>(mode, coef, dk, dv, p, st);
-  if (act == DT_BF16 && sketch == DT_BF16) return launch_dtype<FAM, bf16, bf16>(mode, coef, dk, dv, p, st);
-  return -3;
-}
 
 }  // namespace sk

@@ -1,0 +1,8 @@
+// Kernel instantiations of one family for fp32 activations and sketch.
+#include "sk_dispatch.hpp"
+
+namespace sk {
+int launch_gdn_f32(int mode, int coef, int dk, int dv, const Params& p, hipStream_t st) {
+  return launch_dtype<FAM_GDN, float, float>(mode, coef, dk, dv, p, st);
+}
+}  // namespace sk

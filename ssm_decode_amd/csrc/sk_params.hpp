@@ -18,8 +18,8 @@ struct Params {
   int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
   const int32_t* seq_list;  // MODE_FLUSH: device list of nseq sequences to flush, or null (all)
   int nseq;
-  int* due_work;        // MODE_FLUSH with a device-side due list: its part of the workspace
-  int due_nreg;         //   and the number of tile regions (0: no list)
+  const int32_t* seq_count;  // MODE_FLUSH, device-side due list: the list's length (device), or null
+  int* due_work;        // the due list's workspace (scan launch: the sequences whose ring is full)
   float* S;
   void* U;
   const float* Pt;
@@ -75,23 +75,22 @@ struct DnWork {
   }
 };
 
-// Due tiles listed on the device for a flush (SKSSM_FLUSH_DUE_SCAN): the
-// tiles (b * H + h) are split into regions of DUE_RT consecutive tiles; a
-// region's due tiles are listed in its own slice of the workspace, after
-// every region's number of them (int32 offsets).
-constexpr int DUE_RT = 1024;       // tiles per region: 16 per lane of one wave
-
+// Due sequences listed on the device for a flush (SKSSM_FLUSH_DUE_SCAN):
+// the number of them, then the list (int32 offsets in the workspace).
 struct DueWork {
   size_t cnt, list, total;
-  __host__ __device__ DueWork(int B, int H) {
-    const size_t nreg = ((size_t)B * H + DUE_RT - 1) / DUE_RT;
+  __host__ __device__ explicit DueWork(int B) {
     cnt = 0;
-    list = (nreg + 63) / 64 * 64;
-    total = list + nreg * DUE_RT;
+    list = 64;
+    total = list + ((size_t)B + 63) / 64 * 64;
   }
 };
-__host__ __device__ inline int due_regions(int B, int H) {
-  return (int)(((size_t)B * H + DUE_RT - 1) / DUE_RT);
+// Sequences the one-tile-per-workgroup launch of a scan flush covers: twice
+// the expected number of due sequences under a uniformly ragged phase, plus
+// a margin; the rest go to a small looping launch.
+__host__ __device__ inline int due_slots(int B, int W) {
+  const int s = 2 * ((B + W - 1) / W) + 8;
+  return s < B ? s : B;
 }
 
 // Position of dense-fallback head h in the list (h must be listed).

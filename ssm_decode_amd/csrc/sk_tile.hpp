@@ -323,60 +323,65 @@ __device__ __forceinline__ void tile_body(const Params& p, const int b, const in
 #undef SK_TILE_BODY_IN_LOOP
 }
 
-// One wave per region: lane l checks tiles base + 64 k + l (k < 16, loads
-// coalesced over the wave), lists those whose ring holds W entries in
-// tile order (ballot and prefix count), and reports counts outside [0, W].
+// One workgroup of 1024 threads lists the sequences whose ring is full
+// (head 0's count == W: every head of a sequence advances together), in
+// sequence order: per chunk of 1024 sequences, a ballot per wave, the
+// waves' totals through LDS, then every due sequence's position.  Head 0
+// counts outside [0, W] are reported (SKSSM_ERRBIT_COUNT).
+constexpr int DUE_SCAN_THREADS = 1024;
+
 template <int UNUSED = 0>
-__global__ void __launch_bounds__(64) due_scan_kernel(Params p) {
-  constexpr int K = DUE_RT / 64;
-  const int lane = threadIdx.x;
-  const int region = blockIdx.x;
-  const int ntiles = p.B * p.H;
-  const size_t base = (size_t)region * DUE_RT;
+__global__ void __launch_bounds__(DUE_SCAN_THREADS) due_scan_kernel(Params p) {
+  constexpr int NW = DUE_SCAN_THREADS / 64;
+  __shared__ int s_wave[NW];
+  __shared__ int s_base;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int* cnt = p.due_work;
-  int* lst = p.due_work + DueWork(p.B, p.H).list + base;
-  int c[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const size_t t = base + 64 * k + lane;
-    c[k] = t < (size_t)ntiles ? p.count[t] : 0;
-  }
-  int n = 0, bad = 0;
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const bool due = c[k] == p.W;
-    bad |= (c[k] < 0 || c[k] > p.W) ? ERRBIT_COUNT : 0;
+  int* lst = p.due_work + DueWork(p.B).list;
+  if (tid == 0) s_base = 0;
+  int bad = 0;
+  for (int b0 = 0; b0 < p.B; b0 += DUE_SCAN_THREADS) {      // uniform
+    const int b = b0 + tid;
+    const int c = b < p.B ? p.count[(size_t)b * p.H] : 0;
+    bad |= (c < 0 || c > p.W) ? ERRBIT_COUNT : 0;
+    const bool due = b < p.B && c == p.W;
     const uint64_t m = __builtin_amdgcn_ballot_w64(due);
-    if (due) lst[n + __popcll(m & below)] = (int)(base + 64 * k + lane);
-    n += __popcll(m);
+    if (lane == 0) s_wave[wv] = __popcll(m);
+    __syncthreads();
+    int before = s_base;                                      // due sequences of earlier waves
+    for (int w = 0; w < wv; ++w) before += s_wave[w];
+    if (due) lst[before + __popcll(m & ((1ull << lane) - 1ull))] = b;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int w = 0; w < NW; ++w) t += s_wave[w];
+      s_base += t;
+    }
+    __syncthreads();
   }
-  if (lane == 0) cnt[region] = n;
-  if (__builtin_amdgcn_ballot_w64(bad != 0) && bad) atomicOr(p.err, bad);
+  if (tid == 0) cnt[0] = s_base;
+  if (bad) atomicOr(p.err, bad);
 }
 
 // (the delta-rule flush runs three waves per SIMD: its chunked update has
 // serial phases that more resident tiles hide)
-// LISTED: the flush over the due tiles listed by due_scan_kernel (its own
-// instantiation: the loop would cost the other kernels registers; it keeps
-// more values live across the body, and runs two waves per SIMD without
-// spills where three would spill).
+// LISTED: the tiles of the sequences listed by due_scan_kernel beyond the
+// first p.nseq, in a loop (its own instantiation: the loop keeps more values
+// live across the body, and runs two waves per SIMD without spills where
+// three would spill; the other tile kernels keep their registers).
 template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX, int COEF, bool DENSE,
           bool LISTED = false>
 __global__ void __launch_bounds__((TileShape<DK, DV>::THREADS),
                                   (MODE == MODE_FLUSH && FAM != FAM_M2 && !LISTED ? 3 : 2))
 tile_kernel(Params p) {
   if constexpr (LISTED) {
-    // workgroup j takes region j mod nreg and every (gridDim / nreg)-th of
-    // the region's listed tiles
-    const int nreg = p.due_nreg;
-    const int region = blockIdx.x % nreg;
-    const int stride = gridDim.x / nreg;
-    const int nd = p.due_work[region];
-    const int* lst = p.due_work + DueWork(p.B, p.H).list + (size_t)region * DUE_RT;
-    for (int it = blockIdx.x / nreg; it < nd; it += stride) {   // uniform
-      const int t = lst[it];
-      tile_body<FAM, DK, DV, AT, UT, MODE, WMAX, COEF, DENSE>(p, t / p.H, t % p.H, -1);
+    // the tiles of the listed sequences past the first p.nseq (which the
+    // one-tile launch covers), every gridDim-th of them per workgroup
+    const size_t first = (size_t)p.nseq * p.H;
+    const size_t end = (size_t)p.seq_count[0] * p.H;
+    for (size_t it = first + blockIdx.x; it < end; it += gridDim.x) {   // uniform
+      const int b = p.seq_list[it / p.H];
+      tile_body<FAM, DK, DV, AT, UT, MODE, WMAX, COEF, DENSE>(p, b, (int)(it % p.H), -1);
     }
   } else {
     const int ts = blockIdx.x / p.H;
@@ -384,6 +389,7 @@ tile_kernel(Params p) {
     int b = ts, n0k = -1;
     if constexpr (MODE == MODE_FLUSH) {
      if (p.seq_list) {                           // uniform: the tiles of listed sequences
+      if (p.seq_count && ts >= p.seq_count[0]) return;   // (a device-side list shorter than the grid)
       b = p.seq_list[ts];
       if (b < 0 || b >= p.B) {
         if (threadIdx.x == 0) atomicOr(p.err, ERRBIT_SEQ);

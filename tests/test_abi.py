@@ -161,16 +161,16 @@ def _m2_work_bytes(B, R, G, W):
 
 
 def _scan_work_bytes(B, H):
-    # the scan flush's due list: per region of 1024 tiles its count (the
-    # counts rounded up to 64 entries), then its 1024-entry list, int32
-    nreg = (B * H + 1023) // 1024
-    return 4 * ((nreg + 63) // 64 * 64 + nreg * 1024)
+    # the scan flush's due list: the number of due sequences (in a first
+    # block of 64 entries), then the list of up to B sequences rounded up to
+    # 64 entries, int32
+    return 4 * (64 + (B + 63) // 64 * 64)
 
 
 def test_workspace_bytes(lib):
     """The workspace is the larger of the read's and the scan flush's needs."""
-    assert _m2_work_bytes(2, 16, 4, 4) == 768 and _scan_work_bytes(2, 4) == 4352
-    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 4352
+    assert _m2_work_bytes(2, 16, 4, 4) == 768 and _scan_work_bytes(2, 4) == 512
+    assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 768
     off = np.concatenate([[0], np.cumsum(np.full(128, 8))]).astype(np.int32)
     L = _layer(off, batch=320, heads=128, groups=8, dk=128, dv=64, W=16)
     assert _m2_work_bytes(320, 1024, 8, 16) > _scan_work_bytes(320, 128)
