@@ -58,6 +58,15 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     """Load the HIP library; raises if it is missing (no CPU fallback)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime under the same soname as the
+        # system's (libamdhip64.so.7); whichever is loaded first serves the
+        # whole process.  Importing torch before the library keeps both on
+        # torch's runtime, so that tensors allocated by torch are valid in
+        # the library's launches whatever the caller imported first.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
                                "(or python ssm_decode_amd/build.py) first")

@@ -2,6 +2,8 @@
 // family's translation unit includes this file once with its own FAMILY.
 #pragma once
 
+#include <atomic>
+
 #include "sk_read.hpp"
 #include "sk_tile.hpp"
 
@@ -10,28 +12,50 @@ namespace sk {
 // Compute units of the current device (cached: the figure only sizes a
 // grid, which is correct at any size).
 static int device_cus() {
-  static int cached = 0;
-  if (cached > 0) return cached;
+  static std::atomic<int> cached{0};
+  const int c = cached.load(std::memory_order_relaxed);
+  if (c > 0) return c;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
     (void)hipGetLastError();
     return 256;
   }
-  cached = cus;
-  return cached;
+  cached.store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Workgroups of a looping kernel that are resident at once on the device:
+// its occupancy per compute unit (registers, LDS, workgroup size) times the
+// compute units, so that the loop runs as many waves per SIMD as one-tile
+// workgroups of the same shape would (cached per kernel; on a failed query,
+// two per compute unit).
+template <void (*K)(Params)>
+static int resident_grid(int threads, size_t lds) {
+  static std::atomic<int> cached{0};
+  const int c = cached.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, lds) != hipSuccess || per_cu <= 0) {
+    (void)hipGetLastError();
+    per_cu = 2;
+  }
+  const int g = per_cu * device_cus();
+  cached.store(g, std::memory_order_relaxed);
+  return g;
 }
 
 // The flush over a device-side list of due sequences: the scan; the
 // one-tile-per-workgroup flush of listed sequences over the first p.nseq
 // list entries (its workgroups past the list's length exit at once); then
-// a looping launch of two workgroups per compute unit for the entries past
-// p.nseq (under a ragged phase usually none: its workgroups exit at once).
+// a looping launch of one round of resident workgroups for the entries
+// past p.nseq (under a ragged phase usually none: its workgroups exit at
+// once).
 template <void (*ONE)(Params), void (*LOOP)(Params)>
 static void launch_scanned_flush(int threads, size_t lds, const Params& p, hipStream_t st) {
   hipLaunchKernelGGL(due_scan_kernel<0>, dim3(1), dim3(DUE_SCAN_THREADS), 0, st, p);
   hipLaunchKernelGGL(ONE, dim3(p.nseq * p.H), dim3(threads), lds, st, p);
-  hipLaunchKernelGGL(LOOP, dim3(2 * device_cus()), dim3(threads), lds, st, p);
+  hipLaunchKernelGGL(LOOP, dim3(resident_grid<LOOP>(threads, lds)), dim3(threads), lds, st, p);
 }
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>

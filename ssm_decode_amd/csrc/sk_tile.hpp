@@ -115,10 +115,14 @@ __device__ __forceinline__ void unpack(const uint4& r, float (&x)[8], const floa
   x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
 }
 
-// Which tile kernels address the state through a buffer resource.
+// Which tile kernels address the state through a buffer resource (one lane
+// offset and immediate row offsets) rather than a 64-bit address per row:
+// the flushes, where the per-row addresses of the state stores would hold
+// 64 VGPRs (the Mamba-2 flush: 98 VGPRs instead of 162, the looping flush
+// over a due list 149 instead of 214).
 template <int FAM, int MODE>
 struct STATE_BUFFER {
-  static constexpr bool value = FAM != FAM_M2 && MODE == MODE_FLUSH;
+  static constexpr bool value = MODE == MODE_FLUSH;
 };
 
 // D += A B for one 16x16x4 fp32 block (A: lane holds A[lane%16][lane/16],

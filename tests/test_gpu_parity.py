@@ -163,7 +163,7 @@ def test_flush_list_stress_w32():
     run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False, flush="list")
 
 
-# ------------- the flush over a device-side list of due tiles vs oracle
+# ------------- the flush over a device-side list of due sequences vs oracle
 @pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
 def test_flush_scan_small_batch(name):
     cfg = CONFIGS[name].with_(name=name + "_scan", batch=5, ragged=True, steps=40)
