@@ -465,12 +465,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2891445509,
-                "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
-    "gdn_b256": {"bytes": 1155942854,
-                 "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
-    "kda_b256": {"bytes": 1213516995,
-                 "src_sha256": "1985d25db045952bcd5d464cde13bb64893759a8b042943941e56ae2222d16ef"},
+    "m2_b320": {"bytes": 2901623582,
+                "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
+    "gdn_b256": {"bytes": 1160291271,
+                 "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
+    "kda_b256": {"bytes": 1222233755,
+                 "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
