@@ -217,13 +217,13 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * sequence together).  A first launch (one workgroup) lists, in sequence
  * order, the sequences whose head-0 count is W in bufs->work
  * (sketchssm_workspace_bytes; 16-byte aligned) and reports head-0 counts
- * outside [0, W] (SKSSM_ERRBIT_COUNT).  The flush then runs a workgroup per
- * tile of the first min(batch, 2 * ceil(batch / W) + 8) listed sequences
- * (about twice what a ragged phase brings due at a step), each tile claimed
- * as in sketchssm_flush_seqs, and a loop over the tiles of any further
- * listed sequences in a grid of two workgroups per compute unit, so that a
- * ragged phase does not pay a workgroup per tile of the batch and an
- * aligned one still flushes every tile.  The counts of the other heads are
+ * outside [0, W] (SKSSM_ERRBIT_COUNT).  The flush then runs a grid of one
+ * workgroup per tile of min(batch, 2 * ceil(batch / W) + 8) sequences
+ * (about twice what a ragged phase brings due at a step) over the tiles of
+ * the listed sequences, each workgroup taking further tiles in turn when
+ * the list is longer (an aligned phase), so that a ragged phase does not
+ * pay a workgroup per tile of the batch.  A listed tile whose count is
+ * below W is left alone; the counts of the other heads are
  * checked in listed sequences only. */
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,

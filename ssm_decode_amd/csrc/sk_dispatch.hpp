@@ -2,60 +2,18 @@
 // family's translation unit includes this file once with its own FAMILY.
 #pragma once
 
-#include <atomic>
-
 #include "sk_read.hpp"
 #include "sk_tile.hpp"
 
 namespace sk {
 
-// Compute units of the current device (cached: the figure only sizes a
-// grid, which is correct at any size).
-static int device_cus() {
-  static std::atomic<int> cached{0};
-  const int c = cached.load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
-    (void)hipGetLastError();
-    return 256;
-  }
-  cached.store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
-// Workgroups of a looping kernel that are resident at once on the device:
-// its occupancy per compute unit (registers, LDS, workgroup size) times the
-// compute units, so that the loop runs as many waves per SIMD as one-tile
-// workgroups of the same shape would (cached per kernel; on a failed query,
-// two per compute unit).
-template <void (*K)(Params)>
-static int resident_grid(int threads, size_t lds) {
-  static std::atomic<int> cached{0};
-  const int c = cached.load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, lds) != hipSuccess || per_cu <= 0) {
-    (void)hipGetLastError();
-    per_cu = 2;
-  }
-  const int g = per_cu * device_cus();
-  cached.store(g, std::memory_order_relaxed);
-  return g;
-}
-
-// The flush over a device-side list of due sequences: the scan; the
-// one-tile-per-workgroup flush of listed sequences over the first p.nseq
-// list entries (its workgroups past the list's length exit at once); then
-// a looping launch of one round of resident workgroups for the entries
-// past p.nseq (under a ragged phase usually none: its workgroups exit at
-// once).
-template <void (*ONE)(Params), void (*LOOP)(Params)>
+// The flush over a device-side list of due sequences: the scan, then the
+// loop over the listed tiles with a workgroup per tile of the first p.nseq
+// list entries (about twice what a ragged phase brings due at a step).
+template <void (*LOOP)(Params)>
 static void launch_scanned_flush(int threads, size_t lds, const Params& p, hipStream_t st) {
   hipLaunchKernelGGL(due_scan_kernel<0>, dim3(1), dim3(DUE_SCAN_THREADS), 0, st, p);
-  hipLaunchKernelGGL(ONE, dim3(p.nseq * p.H), dim3(threads), lds, st, p);
-  hipLaunchKernelGGL(LOOP, dim3(resident_grid<LOOP>(threads, lds)), dim3(threads), lds, st, p);
+  hipLaunchKernelGGL(LOOP, dim3(p.nseq * p.H), dim3(threads), lds, st, p);
 }
 
 template <int FAM, int DK, int DV, typename AT, typename UT, int WMAX>
@@ -70,17 +28,13 @@ static int launch_tile(int mode, int coef, const Params& p, hipStream_t st) {
   if (mode == MODE_FLUSH && p.seq_count) {
     constexpr int NT = TileShape<DK, DV>::THREADS;
     if (coef && dense)
-      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true>,
-                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true, true>>(NT, lds_flush_map, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, true, true>>(NT, lds_flush_map, p, st);
     else if (coef)
-      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false>,
-                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false, true>>(NT, lds_flush_map, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 1, false, true>>(NT, lds_flush_map, p, st);
     else if (dense)
-      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true>,
-                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true, true>>(NT, lds_flush, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, true, true>>(NT, lds_flush, p, st);
     else
-      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false>,
-                           tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false, true>>(NT, lds_flush, p, st);
+      launch_scanned_flush<tile_kernel<FAM, DK, DV, AT, UT, MODE_FLUSH, WMAX, 0, false, true>>(NT, lds_flush, p, st);
     return 0;
   }
   if (mode == MODE_FLUSH && coef && dense)

@@ -85,9 +85,10 @@ struct DueWork {
     total = list + ((size_t)B + 63) / 64 * 64;
   }
 };
-// Sequences the one-tile-per-workgroup launch of a scan flush covers: twice
-// the expected number of due sequences under a uniformly ragged phase, plus
-// a margin; the rest go to a small looping launch.
+// Sequences whose tiles the scan flush's grid covers one workgroup each:
+// twice the expected number of due sequences under a uniformly ragged phase,
+// plus a margin; the grid takes the tiles of any further listed sequences in
+// turn.
 __host__ __device__ inline int due_slots(int B, int W) {
   const int s = 2 * ((B + W - 1) / W) + 8;
   return s < B ? s : B;

@@ -369,21 +369,20 @@ __global__ void __launch_bounds__(DUE_SCAN_THREADS) due_scan_kernel(Params p) {
 
 // (the delta-rule flush runs three waves per SIMD: its chunked update has
 // serial phases that more resident tiles hide)
-// LISTED: the tiles of the sequences listed by due_scan_kernel beyond the
-// first p.nseq, in a loop (its own instantiation: the loop keeps more values
-// live across the body, and runs two waves per SIMD without spills where
-// three would spill; the other tile kernels keep their registers).
+// LISTED: the flush over the device-side list of due sequences written by
+// due_scan_kernel: workgroup g takes tiles g, g + gridDim.x, ... of the
+// listed sequences (tile it = list position * H + head), so that a short
+// list costs a workgroup per tile and a long one (an aligned phase) is
+// taken by the same grid in turn.  Its own instantiation: the loop keeps
+// more values live across the body than the one-tile kernels.
 template <int FAM, int DK, int DV, typename AT, typename UT, int MODE, int WMAX, int COEF, bool DENSE,
           bool LISTED = false>
 __global__ void __launch_bounds__((TileShape<DK, DV>::THREADS),
                                   (MODE == MODE_FLUSH && FAM != FAM_M2 && !LISTED ? 3 : 2))
 tile_kernel(Params p) {
   if constexpr (LISTED) {
-    // the tiles of the listed sequences past the first p.nseq (which the
-    // one-tile launch covers), every gridDim-th of them per workgroup
-    const size_t first = (size_t)p.nseq * p.H;
     const size_t end = (size_t)p.seq_count[0] * p.H;
-    for (size_t it = first + blockIdx.x; it < end; it += gridDim.x) {   // uniform
+    for (size_t it = blockIdx.x; it < end; it += gridDim.x) {   // uniform
       const int b = p.seq_list[it / p.H];
       tile_body<FAM, DK, DV, AT, UT, MODE, WMAX, COEF, DENSE>(p, b, (int)(it % p.H), -1);
     }
@@ -393,7 +392,6 @@ tile_kernel(Params p) {
     int b = ts, n0k = -1;
     if constexpr (MODE == MODE_FLUSH) {
      if (p.seq_list) {                           // uniform: the tiles of listed sequences
-      if (p.seq_count && ts >= p.seq_count[0]) return;   // (a device-side list shorter than the grid)
       b = p.seq_list[ts];
       if (b < 0 || b >= p.B) {
         if (threadIdx.x == 0) atomicOr(p.err, ERRBIT_SEQ);
