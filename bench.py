@@ -465,12 +465,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2901623582,
-                "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
-    "gdn_b256": {"bytes": 1160291271,
-                 "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
-    "kda_b256": {"bytes": 1222233755,
-                 "src_sha256": "4e3a65eb44ea3b97ee56af702811569df46a0b75bc0c64441282cbfb931de2bc"},
+    "m2_b320": {"bytes": 2901618090,
+                "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
+    "gdn_b256": {"bytes": 1160295761,
+                 "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
+    "kda_b256": {"bytes": 1222230057,
+                 "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
