@@ -3,9 +3,11 @@ A captured sequence of reads and flushes, replayed, must give bit-identical
 outputs, states, sketches, maps, state copies, rings, counts and error word
 to the same calls made eagerly, on every replay, with the program's own
 eager work (restoring the buffers) between the replays.  The flush is the
-due-flag flush, or the flush of listed sequences with each step's due
-sequences (device lists made before the capture; the eager listed run is
-also checked against the eager due-flag run)."""
+due-flag flush, the flush of listed sequences with each step's due
+sequences (device lists made before the capture), or the flush over the
+device-side due list (SKSSM_FLUSH_DUE_SCAN, whose list and count live in
+the workspace); the eager listed and scanned runs are also checked against
+the eager due-flag run."""
 import pytest
 
 from synth import CONFIGS
@@ -36,6 +38,11 @@ CASES = [
     ("kda_b256", dict(batch=2, ragged=True), "state", "serial", "due"),
     ("m2_b320", dict(batch=5, ragged=True), "fixed", "serial", "list"),
     ("kda_b256", dict(batch=3, ragged=True), "state", "serial", "list"),
+    ("m2_b320", dict(batch=5, ragged=True), "fixed", "serial", "scan"),
+    ("gdn_b256", dict(batch=3, ragged=True, dense_heads=(1,)), "fixed", "serial", "scan"),
+    # aligned, 64 sequences due at once: more than the scan flush's grid
+    # covers one workgroup each, so its workgroups take several tiles
+    ("tiny_m2", dict(batch=64), "fixed", "serial", "scan"),
 ]
 
 
@@ -73,6 +80,8 @@ def test_graph_replay_matches_eager(name, over, coef, pullback, flush):
             assert lay.read(st, stream=stream) == 0
             if mode == "list":
                 assert lay.flush_seqs(st, lists[t], stream=stream) == 0
+            elif mode == "scan":
+                assert lay.flush(st, abi.SKSSM_FLUSH_DUE_SCAN, stream=stream) == 0
             else:
                 assert lay.flush(st, abi.SKSSM_FLUSH_DUE, stream=stream) == 0
 
@@ -80,15 +89,15 @@ def test_graph_replay_matches_eager(name, over, coef, pullback, flush):
     torch.cuda.synchronize()
     eager_o = [st.o.clone() for st in steps]
     eager_b = {n: b.clone() for n, b in _buffers(lay).items()}
-    if flush == "list":                        # the lists name exactly the due sequences
+    if flush in ("list", "scan"):              # the same tiles as the due-flag flush
         assert (c0 == c0[:, :1]).all()
         restore()
         run(None, "due")
         torch.cuda.synchronize()
         for t, st in enumerate(steps):
-            assert torch.equal(st.o, eager_o[t]), ("due vs list", t)
+            assert torch.equal(st.o, eager_o[t]), ("due vs " + flush, t)
         for n, b in _buffers(lay).items():
-            assert torch.equal(b, eager_b[n]), ("due vs list", n)
+            assert torch.equal(b, eager_b[n]), ("due vs " + flush, n)
 
     restore()
     torch.cuda.synchronize()
