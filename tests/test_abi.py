@@ -160,7 +160,7 @@ def _m2_work_bytes(B, R, G, W):
     return 4 * (a64(B * R) + a64(B * G * W) + a64(B * G))
 
 
-def _scan_work_bytes(B, H):
+def _scan_work_bytes(B):
     # the scan flush's due list: the number of due sequences (in a first
     # block of 64 entries), then the list of up to B sequences rounded up to
     # 64 entries, int32
@@ -169,17 +169,17 @@ def _scan_work_bytes(B, H):
 
 def test_workspace_bytes(lib):
     """The workspace is the larger of the read's and the scan flush's needs."""
-    assert _m2_work_bytes(2, 16, 4, 4) == 768 and _scan_work_bytes(2, 4) == 512
+    assert _m2_work_bytes(2, 16, 4, 4) == 768 and _scan_work_bytes(2) == 512
     assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, batch=2)) == 768
     off = np.concatenate([[0], np.cumsum(np.full(128, 8))]).astype(np.int32)
     L = _layer(off, batch=320, heads=128, groups=8, dk=128, dv=64, W=16)
-    assert _m2_work_bytes(320, 1024, 8, 16) > _scan_work_bytes(320, 128)
+    assert _m2_work_bytes(320, 1024, 8, 16) > _scan_work_bytes(320)
     assert abi.sketchssm_workspace_bytes(L) == _m2_work_bytes(320, 1024, 8, 16)
     L = _layer(off, batch=1024, heads=128, groups=8, dk=128, dv=64, W=32)
     assert abi.sketchssm_workspace_bytes(L) == max(_m2_work_bytes(1024, 1024, 8, 32),
-                                                   _scan_work_bytes(1024, 128))
+                                                   _scan_work_bytes(1024))
     for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
-        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == _scan_work_bytes(2, 4)
+        assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam)) == _scan_work_bytes(2)
         assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, family=fam, batch=0)) == 0
     assert abi.sketchssm_workspace_bytes(_layer(OK_OFF, W=0)) == abi.SKSSM_EDIM
     assert abi.sketchssm_workspace_bytes(None) == abi.SKSSM_EINVAL
@@ -199,13 +199,13 @@ def test_workspace_bytes_delta_rule_dense_heads(lib):
     for fam in (abi.SKSSM_GDN, abi.SKSSM_KDA):
         L = _layer([0, 4, 4, 8, 8], family=fam, batch=3)          # heads 1 and 3 dense
         assert _dn_work_bytes(3, 2, 16, 32) == 1536
-        assert abi.sketchssm_workspace_bytes(L) == max(1536, _scan_work_bytes(3, 4))
+        assert abi.sketchssm_workspace_bytes(L) == max(1536, _scan_work_bytes(3))
         assert abi.sketchssm_read(L, _bufs(work=None), _step()) == abi.SKSSM_EINVAL
         assert abi.sketchssm_read(L, _bufs(work=FAKE + 4), _step()) == abi.SKSSM_EINVAL
         off = np.concatenate([[0], np.cumsum([0] + [8] * 31)]).astype(np.int32)
         L = _layer(off, family=fam, batch=256, heads=32, groups=32, dk=128, dv=128, W=16)
         assert abi.sketchssm_workspace_bytes(L) == max(_dn_work_bytes(256, 1, 128, 128),
-                                                       _scan_work_bytes(256, 32))
+                                                       _scan_work_bytes(256))
 
 
 def test_read_needs_its_workspace(lib):
@@ -281,7 +281,7 @@ def test_dense_fallback_heads(lib):
     Ld = _layer([0, 0, 0, 0, 0], batch=0)            # every head dense: R = 0
     assert _all_calls(Ld, _bufs(U=None, Pt=None, C=None, Cstate=None), _step()) == [0] * 4
     assert abi.sketchssm_workspace_bytes(_layer([0, 0, 0, 0, 0])) == max(_m2_work_bytes(2, 0, 4, 4),
-                                                                      _scan_work_bytes(2, 4))
+                                                                      _scan_work_bytes(2))
     # at most 64 dense heads per layer
     off = np.concatenate([[0], np.cumsum([0] * 65 + [4] * 63)]).astype(np.int32)
     assert abi.sketchssm_read(_layer(off, heads=128, groups=128, family=abi.SKSSM_GDN, batch=0),
