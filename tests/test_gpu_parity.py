@@ -180,22 +180,25 @@ def test_flush_scan_stress(W, G):
     run(cfg, "sketch", steps=cfg.steps, tiles=tiles, numpy_all=False, flush="scan")
 
 
-def test_flush_scan_aligned_full_batch():
-    """The aligned batch-320 layer (every tile due at once: the listed flush's
-    workgroups each take many tiles) on sampled tiles, three windows."""
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
+def test_flush_scan_aligned_full_batch(name):
+    """The aligned full-batch layers (every tile due at once: the scan
+    flush's workgroups each take several tiles) on sampled tiles, three
+    windows."""
     from tests.gpu_parity import sample_tiles
-    cfg = CONFIGS["m2_b320"]
+    cfg = CONFIGS[name]
     run(cfg, "sketch", steps=3 * cfg.window, tiles=sample_tiles(cfg, 4, 4, seed=cfg.seed + 1),
         numpy_all=False, flush="scan")
 
 
 # ------------- the delta rule's 32-slot chunked flush at the real head shape
-@pytest.mark.parametrize("flush", ["due", "list"])
+@pytest.mark.parametrize("flush", ["due", "list", "scan"])
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
 def test_delta_rule_w32_real_heads(name, flush):
     """dk = dv = 128 with W = 32: the chunked flush applies 32 entries (two
     16-entry blocks of the triangular system), every tile, ragged phases,
-    2W + 3 steps."""
+    2W + 3 steps; through the due-flag flush, the caller's list and the
+    device-side due list."""
     cfg = CONFIGS[name].with_(name=name + "_w32", batch=3, window=32, ragged=True, steps=67)
     run(cfg, "sketch", flush=flush)
 
