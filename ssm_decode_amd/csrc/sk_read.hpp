@@ -232,10 +232,11 @@ __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
   *reinterpret_cast<VecN<T, N>*>(p) = x;
 }
 
-// Sketched read: one wave per (sequence, group, block of M2R_HPW heads),
-// M2R_WPB consecutive such waves a workgroup, 16 lanes per head (one DPP
-// row).  Lane s of a head holds ring slots s*SPL..
-// for the decay scan, coefficient j = s, and output columns s*CPL.. .  The
+// Sketched read: one wave per (sequence, group, block of 4 / CS heads),
+// M2R_WPB consecutive such waves a workgroup, CS rows of 16 lanes per head
+// (DPP rows; each row takes dv / CS of the head's columns and repeats the
+// head's per-slot work).  Lane s of a row holds ring slots s*SPL..
+// for the decay scan, coefficient j = s, and CPL output columns.  The
 // ring fill comes from the prep kernel's workspace; then every load is
 // issued before the first wait: slot gates and dot products, the head's cq
 // entry, then the head's r sketch rows and n0 ring values (the lean kernel
@@ -243,35 +244,54 @@ __device__ __forceinline__ void stv(T* p, const VecN<T, N>& x) {
 // not issued).  The per-slot coefficients w_i d_i and the cq entries are
 // exchanged within the head's row through LDS (a wave reads what its own
 // lanes wrote).
-constexpr int M2R_LPH = 16;        // lanes per head
-constexpr int M2R_HPW = 64 / M2R_LPH;   // heads per wave
+constexpr int M2R_LPH = 16;        // lanes per row of a head
+constexpr int M2R_HPW = 64 / M2R_LPH;   // rows per wave (heads per wave when CS = 1)
 constexpr int M2R_WPB = 4;         // waves per workgroup (measured: 1, 2, 4, 8, 16 -> 4 best)
 
-__host__ __device__ inline int m2_read_items(int B, int G, int HPG) { return B * G * ((HPG + M2R_HPW - 1) / M2R_HPW); }
-inline int m2_read_blocks(int B, int G, int HPG) { return (m2_read_items(B, G, HPG) + M2R_WPB - 1) / M2R_WPB; }
+// 16-lane rows per head (each row takes dv / CS of the head's columns): one
+// row holds at most 4 columns of every sketch row and 2 of every ring row
+// when the ring has 32 slots, so that the loads a lane keeps in flight fit
+// five waves per SIMD (measured at W = 32, dv = 64: 134 -> 87 VGPRs, read
+// call 113.5 -> 110 us at batch 1024)
+constexpr int m2_read_split(int DV, int WMAX) {
+  const int cs = (DV > 64 ? DV / 64 : 1) * (WMAX > 16 ? 2 : 1);
+  return cs < M2R_HPW ? cs : M2R_HPW;
+}
+__host__ __device__ inline int m2_read_items(int B, int G, int HPG, int CS = 1) {
+  const int hpw = M2R_HPW / CS;
+  return B * G * ((HPG + hpw - 1) / hpw);
+}
+inline int m2_read_blocks(int B, int G, int HPG, int CS = 1) {
+  return (m2_read_items(B, G, HPG, CS) + M2R_WPB - 1) / M2R_WPB;
+}
 
-template <int DK, int DV, typename AT, typename UT, int WMAX>
+template <int DK, int DV, typename AT, typename UT, int WMAX, int CS = 1>
 __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
   constexpr int LPH = M2R_LPH;
-  constexpr int HPW = M2R_HPW;
+  constexpr int HPW = M2R_HPW / CS;
   constexpr int SEG = DK / LPH;                  // key elements per lane (append)
-  constexpr int CPL = DV / LPH;                  // output columns per lane
+  constexpr int CPL = DV / (LPH * CS);           // output columns per lane
   constexpr int SPL = WMAX / LPH;                // ring slots per lane in the decay scan
   static_assert(SEG >= 1 && CPL >= 1 && SPL >= 1, "head dims too small for the lane split");
-  __shared__ __align__(16) float s_e_wg[M2R_WPB][HPW * WMAX];  // w_i d_i per head
-  __shared__ __align__(16) float s_c_wg[M2R_WPB][HPW * 16];    // cq entries per head
+  __shared__ __align__(16) float s_e_wg[M2R_WPB][M2R_HPW * WMAX];  // w_i d_i per 16-lane row
+  __shared__ __align__(16) float s_c_wg[M2R_WPB][M2R_HPW * 16];    // cq entries per 16-lane row
   float* s_e = s_e_wg[threadIdx.x >> 6];           // this wave's part
   float* s_c = s_c_wg[threadIdx.x >> 6];
+  // (indexed by the wave's 16-lane row: with CS > 1 the rows of a head hold
+  // the same per-slot values)
 
   const int wpg = (p.HPG + HPW - 1) / HPW;
   // consecutive waves of a workgroup: the head blocks of one (sequence, group)
   const int item = blockIdx.x * M2R_WPB + (threadIdx.x >> 6);
-  if (item >= m2_read_items(p.B, p.G, p.HPG)) return;
+  if (item >= m2_read_items(p.B, p.G, p.HPG, CS)) return;
   const int bgi = item / wpg;
   const int wq = item - bgi * wpg;
   const int tid = threadIdx.x & 63;
-  const int hh = tid >> 4;                       // head row of the wave
+  const int rr = tid >> 4;                       // 16-lane row of the wave
+  const int hh = rr / CS;                        // head of the wave
+  const int cs = rr - hh * CS;                   // its column part
   const int s = tid & 15;
+  const int col0 = cs * (DV / CS) + s * CPL;     // first of the lane's output columns
   const int W = p.W, HPG = p.HPG;
   const int b = bgi / p.G;
   const int g = bgi - b * p.G;
@@ -300,7 +320,7 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
 
   // the step's own entry (kept for the append)
   const VecN<AT, SEG> kcur = ldraw<SEG>(kin + s * SEG);
-  const VecN<AT, CPL> vcur = ldraw<CPL>(vin + s * CPL);
+  const VecN<AT, CPL> vcur = ldraw<CPL>(vin + col0);
   const AT dtcur = dtin[0];
 
   if (n < W && n0c >= 0) {                       // uniform
@@ -315,12 +335,12 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
     }
     const float cqv = reinterpret_cast<const float*>(p.work)[(size_t)b * p.R + off + (s < r ? s : 0)];
     VecN<UT, CPL> us[16];
-    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + s * CPL;
+    const UT* Ur = reinterpret_cast<const UT*>(p.U) + ((size_t)b * p.R + off) * DV + col0;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (j < r) us[j] = ldraw_nt<CPL>(Ur + (size_t)j * DV);
     VecN<AT, CPL> vs[WMAX];
-    const AT* rv0 = ring_v + s * CPL;
+    const AT* rv0 = ring_v + col0;
 #pragma unroll
     for (int i = 0; i < WMAX - 1; ++i)
       if (i < n0) vs[i] = ldraw_nt<CPL>(rv0 + (size_t)i * DV);
@@ -343,8 +363,8 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
     incl *= dpp_f<0x108>(incl, 1.f);
     const float after = dpp_f<0x101>(incl, 1.f); // prod over lanes > s
     const float D = row16_prod(lp);
-    float* eh = s_e + hh * WMAX;
-    float* ch = s_c + hh * 16;
+    float* eh = s_e + rr * WMAX;
+    float* ch = s_c + rr * 16;
     {
       float suf = after;
 #pragma unroll
@@ -386,7 +406,7 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) out[c] = D * acc[c] + ob[c];
     // (a dense-fallback head's output comes from m2_dense_read_kernel)
-    if (hv && r > 0) stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + s * CPL, out);
+    if (hv && r > 0) stn<CPL>(reinterpret_cast<AT*>(p.o) + bh * DV + col0, out);
   }
   if (n0c < 0) {                                 // the prep kernel found a bad group
     if (tid == 0 && wq == 0) atomicOr(p.err, -n0c);
@@ -396,10 +416,10 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
   // ------------------------------------------------------------ append
   AT* rk = reinterpret_cast<AT*>(p.rk) + (bg * W + n0) * DK;
   AT* rv = reinterpret_cast<AT*>(p.rv) + (bh * W + n0) * DV;
-  if (wq == 0 && hh == 0) stv<SEG>(rk + s * SEG, kcur);
+  if (wq == 0 && rr == 0) stv<SEG>(rk + s * SEG, kcur);
   if (hv) {
-    stv<CPL>(rv + s * CPL, vcur);
-    if (s == 0) {
+    stv<CPL>(rv + col0, vcur);
+    if (s == 0 && cs == 0) {
       reinterpret_cast<AT*>(p.rg)[bh * W + n0] = dtcur;
       p.count[bh] = n;
     }

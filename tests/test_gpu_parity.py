@@ -100,6 +100,17 @@ def test_small_batch_ragged(name):
     run(cfg, "sketch")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("W", [16, 32])
+def test_m2_other_head_shapes(dk, dv, W):
+    """Mamba-2 at the other supported head shapes, both ring capacities,
+    every tile, ragged: the read splits a head's columns over two or four
+    16-lane rows where its loads would not fit five waves per SIMD (128
+    columns, or a 32-slot ring)."""
+    cfg = _small("m2_b320", batch=3, ragged=True, steps=2 * W + 5, dk=dk, dv=dv, window=W)
+    run(cfg, "sketch")
+
+
 @pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("method", ["replay", "standard"])
 def test_small_batch_baselines(name, method):
