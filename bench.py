@@ -465,12 +465,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2901618090,
-                "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
-    "gdn_b256": {"bytes": 1160295761,
-                 "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
-    "kda_b256": {"bytes": 1222230057,
-                 "src_sha256": "7374e94f94949fe3b2fb2e2a9735262609ae33d7981c8819106567007b54529e"},
+    "m2_b320": {"bytes": 2901620168,
+                "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
+    "gdn_b256": {"bytes": 1160296682,
+                 "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
+    "kda_b256": {"bytes": 1222232543,
+                 "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
