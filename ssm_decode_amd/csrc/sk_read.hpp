@@ -433,7 +433,9 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
 // with the dot products d_i and the checked ring fill from the prep
 // kernel's workspace.  The head's state copy is read in one pass, every
 // 16-byte chunk in flight at once: lane l takes chunk l % LPRW of rows
-// l / LPRW + RPP i, and the lanes of a chunk column are summed at the end.
+// l / LPRW + RPP i, and of ring rows l / LPRW + RPP k (the ring rows of a
+// chunk column spread over its lanes as the state rows are), and the lanes
+// of a chunk column are summed at the end.
 template <int DK, int DV, typename AT, typename UT, int WMAX>
 __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   constexpr int CE = 16 / (int)sizeof(UT);           // elements per chunk
@@ -470,10 +472,13 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   const float* dws = reinterpret_cast<const float*>(p.work) + wl.d + bg * W;
   const float dl = dws[lane <= n0 ? lane : 0];
   const AT* ring_v = reinterpret_cast<const AT*>(p.rv) + bh * W * DV + cc * CE;
-  VecN<AT, CE> vs[WMAX];
+  constexpr int RPL = (WMAX - 1 + RPP - 1) / RPP;   // ring rows per lane
+  VecN<AT, CE> vs[RPL];
 #pragma unroll
-  for (int i = 0; i < WMAX - 1; ++i)
-    if (i < n0) vs[i] = ldraw_nt<CE>(ring_v + (size_t)i * DV);
+  for (int k = 0; k < RPL; ++k) {                  // (rows past the fill: row 0, weighted 0 below)
+    const int i = r0 + RPP * k;
+    vs[k] = ldraw_nt<CE>(ring_v + (size_t)(i < n0 ? i : 0) * DV);
+  }
   const VecN<AT, CE> vcur = ldraw<CE>(reinterpret_cast<const AT*>(p.v) + bh * DV + cc * CE);
 
   // decays: a_i = exp(-dt_i e^A), w_i = dt_i prod_{t>i} a_t, D = prod_t a_t
@@ -488,9 +493,10 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
   const float e = lane < n ? dt * (lane + 1 < 64 ? excl : 1.0f) * dl : 0.f;   // w_i d_i
   const float D = lane_value(suf, 0);
 
-  // Scopy^T q over this lane's rows, then over the lanes of its chunk column
+  // Scopy^T q and the buffered term over this lane's rows, then over the
+  // lanes of its chunk column
   __syncthreads();
-  float acc[CE];
+  float acc[CE], ob[CE];
 #pragma unroll
   for (int c = 0; c < CE; ++c) acc[c] = 0.f;
 #pragma unroll
@@ -499,28 +505,25 @@ __global__ void __launch_bounds__(64) m2_dense_read_kernel(Params p) {
 #pragma unroll
     for (int c = 0; c < CE; ++c) acc[c] += qm * vget(sr[i], c);
   }
+  const float en0 = lane_value(e, n0);               // (a readlane: in converged code)
+  const float ecur = r0 == 0 ? en0 : 0.f;            // the step's own entry, once per column
+#pragma unroll
+  for (int c = 0; c < CE; ++c) ob[c] = ecur * vget(vcur, c);
+#pragma unroll
+  for (int k = 0; k < RPL; ++k) {
+    const int i = r0 + RPP * k;
+    const float ei = __shfl(e, i < 64 ? i : 0);
+#pragma unroll
+    for (int c = 0; c < CE; ++c) ob[c] += i < n0 ? ei * vget(vs[k], c) : 0.f;
+  }
+  float out[CE];
+#pragma unroll
+  for (int c = 0; c < CE; ++c) out[c] = D * acc[c] + ob[c];
 #pragma unroll
   for (int m = LPRW; m < 64; m <<= 1)
 #pragma unroll
-    for (int c = 0; c < CE; ++c) acc[c] += __shfl_xor(acc[c], m);
-
-  // the buffered term on the same columns
-  float ob[CE];
-#pragma unroll
-  for (int c = 0; c < CE; ++c) ob[c] = lane_value(e, n0) * vget(vcur, c);
-#pragma unroll
-  for (int i = 0; i < WMAX - 1; ++i)
-    if (i < n0) {
-      const float ei = lane_value(e, i);
-#pragma unroll
-      for (int c = 0; c < CE; ++c) ob[c] += ei * vget(vs[i], c);
-    }
-  if (r0 == 0) {
-    float out[CE];
-#pragma unroll
-    for (int c = 0; c < CE; ++c) out[c] = D * acc[c] + ob[c];
-    stn<CE>(reinterpret_cast<AT*>(p.o) + bh * DV + cc * CE, out);
-  }
+    for (int c = 0; c < CE; ++c) out[c] += __shfl_xor(out[c], m);
+  if (r0 == 0) stn<CE>(reinterpret_cast<AT*>(p.o) + bh * DV + cc * CE, out);
 }
 
 // ------------------------------------------------------------ GDN / KDA

@@ -99,7 +99,7 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     the buffered slots.  flush = "list": the sketch path flushes through
     sketchssm_flush_seqs with each step's due sequences (from the window
     phases) instead of the due-flag flush; flush = "scan": through
-    sketchssm_flush with SKSSM_FLUSH_DUE_SCAN (the due tiles listed on the
+    sketchssm_flush with SKSSM_FLUSH_DUE_SCAN (the due sequences listed on the
     device).
 
     Gates: the relative L2 error pooled over the compared tiles, and the same

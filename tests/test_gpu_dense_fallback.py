@@ -60,6 +60,19 @@ def test_head_64x64(family):
                    dense_heads=(1, 2)))
 
 
+@pytest.mark.parametrize("name,dense", [("m2_b320", (0, 17, 63, 127)), ("gdn_b256", (0, 5)),
+                                        ("kda_b256", (31,))])
+def test_window_32(name, dense):
+    """A 32-slot ring: the dense reads take up to 31 buffered entries."""
+    run(CONFIGS[name].with_(name=name + "_dense_w32", batch=3, ragged=True, window=32, steps=69,
+                            dense_heads=dense))
+
+
+def test_m2_head_128x128():
+    run(CONFIGS["m2_b320"].with_(name="m2_128x128_dense", dk=128, dv=128, batch=2, steps=36, ragged=True,
+                                 dense_heads=(3, 64)))
+
+
 def test_state_map():
     run(CONFIGS["kda_b256"].with_(name="kda_dense_map", batch=2, ragged=True, steps=24,
                                   dense_heads=(3, 4)), coef="state")

@@ -181,6 +181,20 @@ def test_flush_scan_small_batch(name):
     run(cfg, "sketch", flush="scan")
 
 
+def test_flush_scan_batch_over_one_scan_chunk():
+    """A batch of 2,500 sequences: the scan lists the due sequences over
+    three chunks of 1,024 (a running base carried between chunks); small
+    heads, ragged, W = 4, sampled tiles in every chunk."""
+    import numpy as np
+    from synth import LayerConfig
+    cfg = LayerConfig(name="tiny_m2_b2500_scan", family="mamba2", batch=2500, heads=4, qk_groups=4, dk=16,
+                      dv=32, window=4, mean_rank=4, fixed_rank=4, act="bf16", sketch="bf16", steps=14,
+                      ragged=True, seed=91)
+    tiles = np.array([(b, h) for b in (0, 1, 1023, 1024, 1500, 2047, 2048, 2499) for h in (0, 3)],
+                     dtype=np.int64)
+    run(cfg, "sketch", tiles=tiles, numpy_all=False, flush="scan")
+
+
 @pytest.mark.parametrize("W,G", [(32, 8), (8, 16)])
 def test_flush_scan_stress(W, G):
     """Batch 1024, ragged, flushed through SKSSM_FLUSH_DUE_SCAN for the full
