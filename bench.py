@@ -50,7 +50,11 @@ def parse():
     ap.add_argument("--flush-list", action="store_true",
                     help="ragged phase: flush through sketchssm_flush_seqs with each step's due sequences")
     ap.add_argument("--flush-scan", action="store_true",
-                    help="flush with SKSSM_FLUSH_DUE_SCAN (the due tiles listed on the device)")
+                    help="flush with SKSSM_FLUSH_DUE_SCAN (the due sequences listed on the device; "
+                         "the default under a ragged phase)")
+    ap.add_argument("--flush-due", action="store_true",
+                    help="flush with SKSSM_FLUSH_DUE (a workgroup per tile of the batch; the default "
+                         "under an aligned phase)")
     ap.add_argument("--no-wy", action="store_true",
                     help="skip the GDN/KDA run with the triangular-system pull-back")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
@@ -140,6 +144,10 @@ def main():
     REPS = max(5, args.reps)
     # listed flush: the sequences whose window closes at step t (t mod W),
     # from each sequence's initial ring fill; device-resident for the graph
+    # the flush: the caller's list, the device-side due list or the due
+    # flag; by default the due list under a ragged phase (the flush for a
+    # caller that does not track phases) and the due flag under an aligned one
+    use_scan = args.flush_scan or (ragged and not args.flush_due and not args.flush_list)
     flush_lists = None
     if args.flush_list and ragged:
         c0 = np.asarray(li.count0)
@@ -176,7 +184,7 @@ def main():
                                                       int(dl.numel()), sh_)
                     else:
                         rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st,
-                                                 abi.SKSSM_FLUSH_DUE_SCAN if args.flush_scan
+                                                 abi.SKSSM_FLUSH_DUE_SCAN if use_scan
                                                  else abi.SKSSM_FLUSH_DUE, sh_)
                     if ev is not None:
                         ev["flush"][-1][1].record(stream)
@@ -423,7 +431,7 @@ def main():
             "mean_rank": cfg.mean_rank, "state": "f32", "act": cfg.act, "sketch": cfg.sketch,
             "layers_rotated": L, "windows_exact": windows_exact,
             "flush": ("listed sequences (sketchssm_flush_seqs)" if flush_lists is not None else
-                      "due tiles listed on the device (SKSSM_FLUSH_DUE_SCAN)" if args.flush_scan
+                      "due sequences listed on the device (SKSSM_FLUSH_DUE_SCAN)" if use_scan
                       else "due flag"),
         },
         "achieved_gbs": round(achieved_gbs, 1),
