@@ -125,6 +125,28 @@ def test_mamba2_closed_form():
     assert rel(lay.S[0], ref) < TOL
 
 
+def test_mamba2_decay_special_values():
+    """The Mamba-2 decay at values known without its formula: with
+    exp(A) = ln 2 a step of gate dt decays the state by 2^-dt, and gate 0
+    leaves it unchanged and writes nothing.  S0 = I (2 x 2), one-hot keys
+    and values, a window of three steps (dt = 1, 0, 2):
+      after dt = 1, k = e0, v = e1:  S = [[1/2, 1], [0, 1/2]]
+      after dt = 0:                  unchanged
+      after dt = 2, k = e1, v = e0:  S = [[1/8, 1/4], [2, 1/8]]
+    and the flush step's output for q = (1, 1) is S^T q = (17/8, 3/8)."""
+    dk = dv = 2
+    A = float(np.log(np.log(2.0)))
+    e0, e1 = np.array([1.0, 0.0]), np.array([0.0, 1.0])
+    q = np.array([1.0, 1.0])
+    ents = [(q, e0, e1, 1.0, 0.0), (q, e0, e1, 0.0, 0.0), (q, e1, e0, 2.0, 0.0)]
+    Pt = np.eye(2)
+    lay = single_tile("mamba2", dk, dv, 3, np.eye(2), Pt, Pt.copy(), A)
+    outs, _, _ = run_sketch(lay, [entry_step("mamba2", e) for e in ents])
+    want = np.array([[0.125, 0.25], [2.0, 0.125]])
+    assert np.abs(lay.S[0] - want).max() < 1e-14
+    assert np.abs(outs[2][0] - np.array([2.125, 0.375])).max() < 1e-14
+
+
 @pytest.mark.parametrize("r", [1, 2, 3])
 def test_mamba2_span_pin(r):
     """P4: for Mamba-2 q~ is a scalar multiple of q, so if every query lies in
