@@ -140,7 +140,7 @@ def main():
     # the timed steps are whole windows: every window of a layer is one flush
     # and W - 1 reads, so the per-step figure is W-amortised exactly
     K_req = args.steps
-    K = max(W, -(-K_req // W) * W)
+    K = timed_steps(K_req, W)
     REPS = max(5, args.reps)
     # listed flush: the sequences whose window closes at step t (t mod W),
     # from each sequence's initial ring fill; device-resident for the graph
@@ -482,6 +482,13 @@ TRAFFIC = {
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
+
+
+def timed_steps(k_req: int, window: int) -> int:
+    """The steps timed for a request of k_req: rounded up to whole windows,
+    at least one window, so that every layer's window (one flush, W - 1
+    reads) is timed whole."""
+    return max(window, -(-k_req // window) * window)
 
 
 def flush_src_digest():
