@@ -181,6 +181,18 @@ def test_flush_scan_small_batch(name):
     run(cfg, "sketch", flush="scan")
 
 
+def test_flush_scan_state_map_and_dense_heads():
+    """The scan flush's other instantiations: the state-dependent map (KDA)
+    and layers with dense-fallback heads (Mamba-2, GDN), ragged, every
+    tile."""
+    run(CONFIGS["kda_b256"].with_(name="kda_scan_map", batch=3, ragged=True, steps=36), "sketch",
+        coef="state", flush="scan")
+    run(CONFIGS["m2_b320"].with_(name="m2_scan_dense", batch=3, ragged=True, steps=36,
+                                 dense_heads=(0, 77)), "sketch", flush="scan")
+    run(CONFIGS["gdn_b256"].with_(name="gdn_scan_dense", batch=3, ragged=True, steps=36,
+                                  dense_heads=(5,)), "sketch", flush="scan")
+
+
 def test_flush_scan_batch_over_one_scan_chunk():
     """A batch of 2,500 sequences: the scan lists the due sequences over
     three chunks of 1,024 (a running base carried between chunks); small
