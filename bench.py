@@ -457,6 +457,16 @@ def main():
             "traffic_unit": "HBM bytes per flush launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
                             "copy-calibrated); null when the flush kernel changed since",
         },
+        # the non-flush read call (every kernel of sketchssm_read), the
+        # other kernel of the step, against the same peak
+        "roofline_read": {
+            "bound": "hbm", "kernel": "read call", "achieved": round(read_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(read_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(cfg.name),
+            "traffic_unit": "HBM bytes per read call, averaged over the window's calls (rocprofv3 "
+                            "FETCH_SIZE x2 + WRITE_SIZE x1 of every read kernel); null when a read "
+                            "kernel changed since",
+        },
         "baselines": baselines,
         "sketch_error": approx,
         "state_map": state_map,
@@ -491,13 +501,40 @@ def timed_steps(k_req: int, window: int) -> int:
     return max(window, -(-k_req // window) * window)
 
 
-def flush_src_digest():
+# HBM bytes per read call (every kernel of sketchssm_read; mean over the
+# window's calls) from the same counter runs, with the digest of the read
+# kernels' sources at that time.
+TRAFFIC_READ = {
+    "m2_b320": {"bytes": 108168339, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
+    "gdn_b256": {"bytes": 59668346, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
+    "kda_b256": {"bytes": 94045281, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
+}
+READ_SOURCES = ("sk_read.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
+                "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
+
+
+def _digest(files):
     import hashlib
     h = hashlib.sha256()
-    for f in FLUSH_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "ssm_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def read_traffic(name):
+    e = TRAFFIC_READ.get(name)
+    if e is None or e["src_sha256"] != read_src_digest():
+        return None
+    return e["bytes"]
+
+
+def flush_src_digest():
+    return _digest(FLUSH_SOURCES)
+
+
+def read_src_digest():
+    return _digest(READ_SOURCES)
 
 
 def flush_traffic(name):

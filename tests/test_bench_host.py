@@ -40,6 +40,22 @@ def test_traffic_reported_only_for_the_measured_sources(monkeypatch):
     assert bench.flush_traffic("no_such_workload") is None
 
 
+def test_read_traffic_reported_only_for_the_measured_sources(monkeypatch):
+    digest = bench.read_src_digest()
+    assert len(digest) == 64 and digest != bench.flush_src_digest()
+    for f in bench.READ_SOURCES:
+        assert os.path.exists(os.path.join(ROOT, "ssm_decode_amd", "csrc", f)), f
+    assert "sk_read.hpp" in bench.READ_SOURCES
+    monkeypatch.setitem(bench.TRAFFIC_READ, "probe", {"bytes": 7, "src_sha256": digest})
+    assert bench.read_traffic("probe") == 7
+    monkeypatch.setitem(bench.TRAFFIC_READ, "probe", {"bytes": 7, "src_sha256": "0" * 64})
+    assert bench.read_traffic("probe") is None
+    assert bench.read_traffic("no_such_workload") is None
+    # the stored figures are for the sources as they stand
+    for name in ("m2_b320", "gdn_b256", "kda_b256"):
+        assert bench.read_traffic(name) == bench.TRAFFIC_READ[name]["bytes"]
+
+
 def test_cpu_model_is_named():
     m = bench.cpu_model()
     assert isinstance(m, str) and m
