@@ -53,8 +53,9 @@ def parse():
                     help="flush with SKSSM_FLUSH_DUE_SCAN (the due sequences listed on the device; "
                          "the default under a ragged phase)")
     ap.add_argument("--flush-due", action="store_true",
-                    help="flush with SKSSM_FLUSH_DUE (a workgroup per tile of the batch; the default "
-                         "under an aligned phase)")
+                    help="flush with SKSSM_FLUSH_DUE after every step's read (a workgroup per tile of "
+                         "the batch); under an aligned phase the default is SKSSM_FLUSH_CLOSE at the "
+                         "closing step, in place of its read")
     ap.add_argument("--no-wy", action="store_true",
                     help="skip the GDN/KDA run with the triangular-system pull-back")
     ap.add_argument("--cpu-seqs", type=int, default=320, help="sequences in the CPU sample")
@@ -148,6 +149,10 @@ def main():
     # flag; by default the due list under a ragged phase (the flush for a
     # caller that does not track phases) and the due flag under an aligned one
     use_scan = args.flush_scan or (ragged and not args.flush_due and not args.flush_list)
+    # an aligned phase: the step that closes every window is one closing
+    # flush (SKSSM_FLUSH_CLOSE), whose read would only append
+    use_close = not ragged and not (args.flush_due or args.flush_list or args.flush_scan)
+    reads_per_window = W - 1 if use_close else W
     flush_lists = None
     if args.flush_list and ragged:
         c0 = np.asarray(li.count0)
@@ -166,6 +171,15 @@ def main():
             due = ragged or ((t - phase) % W == 0)
             for l, lay in enumerate(layers):
                 st = steps_structs[t % P][l]
+                if use_close and due:
+                    if ev is not None:
+                        ev["flush"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        ev["flush"][-1][0].record(stream)
+                    rc = abi.sketchssm_flush(lay.layer_struct, lay.buffers_struct, st, abi.SKSSM_FLUSH_CLOSE, sh_)
+                    if ev is not None:
+                        ev["flush"][-1][1].record(stream)
+                    assert rc == 0
+                    continue
                 if ev is not None:
                     ev["read"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
                     ev["read"][-1][0].record(stream)
@@ -258,7 +272,11 @@ def main():
     flush_bytes = lb.flush_launch if not ragged else \
         (lb.flush_launch - lb.basis) / W + lb.basis
     flush_gbs = flush_bytes / (flush_avg * 1e-6) / 1e9
-    read_gbs = lb.read_launch_avg / (read_avg * 1e-6) / 1e9
+    # bytes of one read call: the window's bytes outside the flush over the
+    # window's read calls (W - 1 with the closing flush, else W, the read at
+    # the closing step appending only)
+    read_bytes = lb.read_launch_avg * W / reads_per_window
+    read_gbs = read_bytes / (read_avg * 1e-6) / 1e9
     windows_exact = K % W == 0
 
     # ------------------------------------------------ GPU baselines
@@ -334,8 +352,9 @@ def main():
             "tokens_per_s_per_layer": round(cfg.batch / (ms["us_per_step"] * 1e-6), 1),
             "flush_us": round(ms["flush_avg"], 2), "flush_bytes": int(round(sflush)),
             "flush_gbs": round(sgbs, 1),
-            "read_us": round(ms["read_avg"], 2), "read_bytes_avg": int(round(lbs.read_launch_avg)),
-            "read_gbs": round(lbs.read_launch_avg / (ms["read_avg"] * 1e-6) / 1e9, 1),
+            "read_us": round(ms["read_avg"], 2),
+            "read_bytes_avg": int(round(lbs.read_launch_avg * W / reads_per_window)),
+            "read_gbs": round(lbs.read_launch_avg * W / reads_per_window / (ms["read_avg"] * 1e-6) / 1e9, 1),
         })
         if baselines:
             sm["speedup_vs_full"] = round(baselines["full_step_us"] / ms["us_per_step"], 3)
@@ -432,7 +451,8 @@ def main():
             "layers_rotated": L, "windows_exact": windows_exact,
             "flush": ("listed sequences (sketchssm_flush_seqs)" if flush_lists is not None else
                       "due sequences listed on the device (SKSSM_FLUSH_DUE_SCAN)" if use_scan
-                      else "due flag"),
+                      else "closing flush in place of the closing step's read (SKSSM_FLUSH_CLOSE)"
+                      if use_close else "due flag"),
         },
         "achieved_gbs": round(achieved_gbs, 1),
         "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -444,7 +464,7 @@ def main():
             "flush_us": round(flush_avg, 2), "flush_launches": len(flush_us),
             "flush_bytes": int(round(flush_bytes)), "flush_gbs": round(flush_gbs, 1),
             "read_us": round(read_avg, 2), "read_launches": len(read_us),
-            "read_bytes_avg": int(round(lb.read_launch_avg)), "read_gbs": round(read_gbs, 1),
+            "read_bytes_avg": int(round(read_bytes)), "read_gbs": round(read_gbs, 1),
             "timing": "eager launches bracketed by HIP events on the launch stream",
         },
         "step_timing": f"{K} steps ({K // W} whole windows) x {L} rotated layers captured in one "
@@ -483,12 +503,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2901620168,
-                "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
-    "gdn_b256": {"bytes": 1160296682,
-                 "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
-    "kda_b256": {"bytes": 1222232543,
-                 "src_sha256": "00237975e732c399175ea7e2aa6a82815ea04a3d449cb44bd7468603aff6db75"},
+    "m2_b320": {"bytes": 2902285504,
+                "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
+    "gdn_b256": {"bytes": 1160797917,
+                 "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
+    "kda_b256": {"bytes": 1222504754,
+                 "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
@@ -505,9 +525,9 @@ def timed_steps(k_req: int, window: int) -> int:
 # window's calls) from the same counter runs, with the digest of the read
 # kernels' sources at that time.
 TRAFFIC_READ = {
-    "m2_b320": {"bytes": 108168339, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
-    "gdn_b256": {"bytes": 59668346, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
-    "kda_b256": {"bytes": 94045281, "src_sha256": "6b82e871fc5256b4418f7402c9ccc796dc748903dd446ddb81fbc1b56392e568"},
+    "m2_b320": {"bytes": 113286211, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
+    "gdn_b256": {"bytes": 62688329, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
+    "kda_b256": {"bytes": 98903509, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
 }
 READ_SOURCES = ("sk_read.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                 "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")

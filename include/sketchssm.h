@@ -98,6 +98,10 @@ extern "C" {
 #define SKSSM_FLUSH_DUE_SCAN 2 /* as SKSSM_FLUSH_DUE, with the due sequences first listed
                                   on the device (in bufs->work), so that a ragged window
                                   phase launches workgroups for the due tiles only */
+#define SKSSM_FLUSH_CLOSE 3 /* the step that closes every tile's window, in place of
+                               sketchssm_read then SKSSM_FLUSH_DUE at that step: tiles
+                               whose ring holds W - 1 entries take the step's own entry
+                               as the W-th */
 
 /* return codes */
 #define SKSSM_OK 0
@@ -224,7 +228,18 @@ int sketchssm_read(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
  * the list is longer (an aligned phase), so that a ragged phase does not
  * pay a workgroup per tile of the batch.  A listed tile whose count is
  * below W is left alone; the counts of the other heads are
- * checked in listed sequences only. */
+ * checked in listed sequences only.
+ * SKSSM_FLUSH_CLOSE (paper App. B: the flush step applies the window's W
+ * entries, its own included, and its output comes from the updated state):
+ * for a step at which every sequence closes its window (an aligned phase),
+ * called instead of sketchssm_read followed by SKSSM_FLUSH_DUE, with the
+ * same results in S, U, count, the maps and o.  step is required (k, v,
+ * gate, beta as for sketchssm_read; q and o for the output).  Each tile's
+ * ring must hold W - 1 entries: the W - 1 buffered entries are applied,
+ * then the step's own, and count becomes 0; a tile with any other count
+ * sets SKSSM_ERRBIT_COUNT and is left untouched (the caller's phase was not
+ * aligned: such a step needs sketchssm_read and SKSSM_FLUSH_DUE).  This
+ * saves the read's launches at the closing step, which only append. */
 int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
                     const sketchssm_step* step /* NULL: no output */, int32_t flags,
                     void* hip_stream);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libsketchssm.so")
 # constants of include/sketchssm.h
 SKSSM_MAMBA2, SKSSM_GDN, SKSSM_KDA = 0, 1, 2
 SKSSM_F32, SKSSM_BF16 = 0, 1
-SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL, SKSSM_FLUSH_DUE_SCAN = 0, 1, 2
+SKSSM_FLUSH_DUE, SKSSM_FLUSH_ALL, SKSSM_FLUSH_DUE_SCAN, SKSSM_FLUSH_CLOSE = 0, 1, 2, 3
 SKSSM_COEF_FIXED, SKSSM_COEF_STATE = 0, 1
 SKSSM_PULLBACK_SERIAL, SKSSM_PULLBACK_WY, SKSSM_PULLBACK_PROJ = 0, 1, 2
 SKSSM_OK, SKSSM_EINVAL, SKSSM_EDIM, SKSSM_EDTYPE, SKSSM_EFLAG, SKSSM_ELAUNCH = 0, -1, -2, -3, -4, -5

@@ -241,15 +241,19 @@ int sketchssm_flush(const sketchssm_layer* layer, const sketchssm_buffers* bufs,
   try {
     int rc = check_layer(layer);
     if (rc) return rc;
-    if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL && flags != SKSSM_FLUSH_DUE_SCAN)
+    if (flags != SKSSM_FLUSH_DUE && flags != SKSSM_FLUSH_ALL && flags != SKSSM_FLUSH_DUE_SCAN &&
+        flags != SKSSM_FLUSH_CLOSE)
       return SKSSM_EFLAG;
+    const bool close = flags == SKSSM_FLUSH_CLOSE;
+    if (close && !step) return SKSSM_EINVAL;     // the step's entry and output are required
     const bool out = step != nullptr;
-    const Needs nd{true, true, true, false, true, true, false, out, out, false, true};
+    const Needs nd{true, true, true, false, true, true, close, out, out, false, true};
     if ((rc = check_buffers(layer, bufs, step, nd))) return rc;
     const bool scan = flags == SKSSM_FLUSH_DUE_SCAN;
     if (scan && layer->batch > 0 && !aligned16(bufs->work)) return SKSSM_EINVAL;
     sk::Params p = make_params(layer, bufs, step);
     p.flush_all = flags == SKSSM_FLUSH_ALL;
+    p.flush_close = close;
     if (scan && layer->batch > 0) {
       p.due_work = static_cast<int*>(bufs->work);
       p.seq_count = p.due_work + sk::DueWork(layer->batch).cnt;

@@ -16,6 +16,8 @@ constexpr int DENSE_LIST_MAX = 64;   // dense-fallback heads listed in the kerne
 struct Params {
   int B, H, G, HPG, W, R;
   int flush_all;        // MODE_FLUSH: flush every tile, not only full rings
+  int flush_close;      // MODE_FLUSH: the step's own entry (k, v, gate, beta) closes
+                        // the window of tiles whose ring holds W - 1 entries
   const int32_t* seq_list;  // MODE_FLUSH: device list of nseq sequences to flush, or null (all)
   int nseq;
   const int32_t* seq_count;  // MODE_FLUSH, device-side due list: the list's length (device), or null

@@ -100,7 +100,9 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
     sketchssm_flush_seqs with each step's due sequences (from the window
     phases) instead of the due-flag flush; flush = "scan": through
     sketchssm_flush with SKSSM_FLUSH_DUE_SCAN (the due sequences listed on the
-    device).
+    device); flush = "close" (aligned phases): the step that closes every
+    window runs sketchssm_flush with SKSSM_FLUSH_CLOSE instead of the read and
+    the due-flag flush (the oracle still reads, then flushes).
 
     Gates: the relative L2 error pooled over the compared tiles, and the same
     error of every tile on its own (o per step; S, U and C per flush).
@@ -173,13 +175,21 @@ def run_parity(cfg, method: str = "sketch", steps: int = None, tiles: np.ndarray
         si = synth.make_step_inputs(cfg, t, b_idx=seqs)
         o_ref = np.zeros((len(tiles), cfg.dv))
         if method == "sketch":
-            assert lay.read(step) == 0
-            if flush == "list":
-                assert lay.flush_seqs(step, due_list(t)) == 0
-            elif flush == "scan":
-                assert lay.flush(step, abi.SKSSM_FLUSH_DUE_SCAN) == 0
+            if flush == "close":
+                assert (li.phase == li.phase[0]).all(), "the closing flush needs an aligned phase"
+                if (t - int(li.phase[0])) % W == 0:    # every window closes at this step
+                    assert lay.flush(step, abi.SKSSM_FLUSH_CLOSE) == 0
+                else:
+                    assert lay.read(step) == 0
             else:
-                assert lay.flush(step, abi.SKSSM_FLUSH_DUE) == 0
+                assert lay.read(step) == 0
+                if flush == "list":
+                    assert lay.flush_seqs(step, due_list(t)) == 0
+                elif flush == "scan":
+                    assert lay.flush(step, abi.SKSSM_FLUSH_DUE_SCAN) == 0
+                else:
+                    assert lay.flush(step, abi.SKSSM_FLUSH_DUE) == 0
+            # (the oracle's window: read, then flush, whatever the HIP path ran)
             rc, _ = orc.read(si, seq_rows=seq_rows, o=o_ref)
             assert rc == 0
             due = orc.count == W

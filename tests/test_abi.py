@@ -137,7 +137,7 @@ def test_null_and_misaligned_pointers(lib):
 
 
 def test_bad_flag(lib):
-    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 3) == abi.SKSSM_EFLAG
+    assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, 4) == abi.SKSSM_EFLAG
     assert abi.sketchssm_flush(_layer(OK_OFF), _bufs(), None, -1) == abi.SKSSM_EFLAG
 
 
@@ -150,6 +150,22 @@ def test_scan_flush_needs_the_workspace(lib):
         assert abi.sketchssm_flush(L, _bufs(work=FAKE + 8), None, abi.SKSSM_FLUSH_DUE_SCAN) == abi.SKSSM_EINVAL
         L0 = _layer(OK_OFF, family=fam, batch=0)
         assert abi.sketchssm_flush(L0, _bufs(work=None), None, abi.SKSSM_FLUSH_DUE_SCAN) == 0
+
+
+def test_closing_flush_needs_the_step(lib):
+    """SKSSM_FLUSH_CLOSE takes the step's own entry and writes its output: no
+    step, or a missing or misaligned key, value, gate (beta for the delta
+    rule), query or output is EINVAL; batch 0 is a no-op."""
+    for fam in (abi.SKSSM_MAMBA2, abi.SKSSM_GDN, abi.SKSSM_KDA):
+        L = _layer(OK_OFF, family=fam)
+        assert abi.sketchssm_flush(L, _bufs(), None, abi.SKSSM_FLUSH_CLOSE) == abi.SKSSM_EINVAL
+        fields = ("k", "v", "gate", "q", "o") + (("beta",) if fam != abi.SKSSM_MAMBA2 else ())
+        for f in fields:
+            for bad in (None, FAKE + 4):
+                assert abi.sketchssm_flush(L, _bufs(), _step(**{f: bad}),
+                                           abi.SKSSM_FLUSH_CLOSE) == abi.SKSSM_EINVAL, (fam, f, bad)
+        L0 = _layer(OK_OFF, family=fam, batch=0)
+        assert abi.sketchssm_flush(L0, _bufs(), _step(), abi.SKSSM_FLUSH_CLOSE) == 0
 
 
 def _m2_work_bytes(B, R, G, W):

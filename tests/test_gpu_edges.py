@@ -1,9 +1,10 @@
 """Edge cases of the HIP path, through the C ABI, against the oracle (needs a
 GPU): a window of one step, the remaining head shape, fp32 activations at
 real head shapes, a flush of every tile in the middle of a window, and the
-device error word for a skipped flush and for heads of one Mamba-2 group
-that disagree on the ring fill (forced from the host; the kernels' own
-checks turn them into error bits and leave the tiles untouched)."""
+device error word for a skipped flush, for a closing flush off phase and for
+heads of one Mamba-2 group that disagree on the ring fill (forced from the
+host; the kernels' own checks turn them into error bits and leave the tiles
+untouched)."""
 import numpy as np
 import pytest
 
@@ -137,6 +138,35 @@ def test_full_ring_read_sets_error(family, seed):
     assert (cnt[0] == W).all() and (cnt[1] == 1).all()
     assert (step.o[0].float().cpu().numpy() == 7.0).all()
     assert not (step.o[1].float().cpu().numpy() == 7.0).all()
+
+
+@pytest.mark.parametrize("family,seed", [("mamba2", 40), ("gdn", 41), ("kda", 42)])
+def test_closing_flush_off_phase_sets_error(family, seed):
+    """SKSSM_FLUSH_CLOSE where a tile's ring does not hold W - 1 entries (the
+    caller's phase was not aligned): that sequence reports
+    SKSSM_ERRBIT_COUNT and keeps its state, count and output; the sequence
+    at W - 1 closes its window (count 0)."""
+    from ssm_decode_amd import abi, feed
+    cfg, lay, step = _primed(family, seed, name=f"close_{family}")
+    W = cfg.window
+    lay.count.zero_()
+    for t in range(W - 1):                  # W - 1 buffered entries in every ring
+        feed.fill_step(step, cfg, t, numpy_all=True)
+        assert lay.read(step) == 0
+    feed.fill_step(step, cfg, W - 1, numpy_all=True)
+    lay.count[1, :] = W - 2                 # sequence 1 off phase
+    S_before = lay.S[1].clone()
+    step.o.fill_(7.0)
+    torch.cuda.synchronize()
+    assert lay.error_word() == 0
+    assert lay.flush(step, abi.SKSSM_FLUSH_CLOSE) == 0
+    torch.cuda.synchronize()
+    assert lay.error_word() & abi.SKSSM_ERRBIT_COUNT
+    cnt = lay.count.cpu().numpy()
+    assert (cnt[0] == 0).all() and (cnt[1] == W - 2).all()
+    assert torch.equal(lay.S[1], S_before)
+    assert (step.o[1].float().cpu().numpy() == 7.0).all()
+    assert not (step.o[0].float().cpu().numpy() == 7.0).all()
 
 
 @pytest.mark.parametrize("family,seed", [("mamba2", 33), ("gdn", 34), ("kda", 35)])

@@ -228,6 +228,43 @@ def test_flush_scan_aligned_full_batch(name):
         numpy_all=False, flush="scan")
 
 
+# ------------- the closing flush: the step that closes every window, without its read
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
+def test_flush_close_small_batch(name):
+    """SKSSM_FLUSH_CLOSE at every closing step of an aligned phase (the
+    step's own entry taken from the step inputs, no read at that step),
+    every tile, 2W + 8 steps; against the oracle's read-then-flush."""
+    cfg = CONFIGS[name].with_(name=name + "_close", batch=3, steps=2 * CONFIGS[name].window + 8)
+    run(cfg, "sketch", flush="close")
+
+
+def test_flush_close_other_instantiations():
+    """The closing flush with the state-dependent map (GDN), with
+    dense-fallback heads (Mamba-2, KDA), with a 32-slot ring at the real
+    delta-rule head shape (GDN) and with W = 1 (Mamba-2: every step closes
+    its window with an empty ring)."""
+    run(CONFIGS["gdn_b256"].with_(name="gdn_close_map", batch=3, steps=36), "sketch",
+        coef="state", flush="close")
+    run(CONFIGS["m2_b320"].with_(name="m2_close_dense", batch=3, steps=36, dense_heads=(0, 77)),
+        "sketch", flush="close")
+    run(CONFIGS["kda_b256"].with_(name="kda_close_dense", batch=3, steps=36, dense_heads=(5,)),
+        "sketch", flush="close")
+    run(CONFIGS["gdn_b256"].with_(name="gdn_close_w32", batch=2, window=32, steps=70), "sketch",
+        flush="close")
+    run(CONFIGS["m2_b320"].with_(name="m2_close_w1", batch=2, window=1, steps=6), "sketch",
+        flush="close")
+
+
+@pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
+def test_flush_close_full_batch(name):
+    """The aligned full-batch layers with the closing flush (the benchmark's
+    configuration) on sampled tiles, three windows."""
+    from tests.gpu_parity import sample_tiles
+    cfg = CONFIGS[name]
+    run(cfg, "sketch", steps=3 * cfg.window, tiles=sample_tiles(cfg, 4, 4, seed=cfg.seed + 3),
+        numpy_all=False, flush="close")
+
+
 # ------------- the delta rule's 32-slot chunked flush at the real head shape
 @pytest.mark.parametrize("flush", ["due", "list", "scan"])
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
