@@ -6,8 +6,11 @@ eager work (restoring the buffers) between the replays.  The flush is the
 due-flag flush, the flush of listed sequences with each step's due
 sequences (device lists made before the capture), or the flush over the
 device-side due list (SKSSM_FLUSH_DUE_SCAN, whose list and count live in
-the workspace); the eager listed and scanned runs are also checked against
-the eager due-flag run."""
+the workspace), or, under an aligned phase, the closing flush
+(SKSSM_FLUSH_CLOSE) in place of the closing step's read; the eager listed,
+scanned and closing runs are also checked against the eager due-flag run
+(the closing run leaves the last ring slot unwritten, so its rings are not
+compared with the due-flag run's)."""
 import pytest
 
 from synth import CONFIGS
@@ -43,6 +46,10 @@ CASES = [
     # aligned, 64 sequences due at once: more than the scan flush's grid
     # covers one workgroup each, so its workgroups take several tiles
     ("tiny_m2", dict(batch=64), "fixed", "serial", "scan"),
+    # aligned phases, the closing step as one closing flush
+    ("m2_b320", dict(batch=3, dense_heads=(5, 70)), "fixed", "serial", "close"),
+    ("gdn_b256", dict(batch=2), "fixed", "serial", "close"),
+    ("kda_b256", dict(batch=2, dense_heads=(1,)), "state", "serial", "close"),
 ]
 
 
@@ -77,6 +84,9 @@ def test_graph_replay_matches_eager(name, over, coef, pullback, flush):
 
     def run(stream, mode=flush):
         for t, st in enumerate(steps):
+            if mode == "close" and (c0[0, 0] + t + 1) % cfg.window == 0:
+                assert lay.flush(st, abi.SKSSM_FLUSH_CLOSE, stream=stream) == 0
+                continue
             assert lay.read(st, stream=stream) == 0
             if mode == "list":
                 assert lay.flush_seqs(st, lists[t], stream=stream) == 0
@@ -89,14 +99,18 @@ def test_graph_replay_matches_eager(name, over, coef, pullback, flush):
     torch.cuda.synchronize()
     eager_o = [st.o.clone() for st in steps]
     eager_b = {n: b.clone() for n, b in _buffers(lay).items()}
-    if flush in ("list", "scan"):              # the same tiles as the due-flag flush
+    if flush in ("list", "scan", "close"):     # the same results as the due-flag flush
         assert (c0 == c0[:, :1]).all()
+        if flush == "close":
+            assert (c0 == c0[0, 0]).all()
         restore()
         run(None, "due")
         torch.cuda.synchronize()
         for t, st in enumerate(steps):
             assert torch.equal(st.o, eager_o[t]), ("due vs " + flush, t)
         for n, b in _buffers(lay).items():
+            if flush == "close" and n.startswith("ring_"):
+                continue
             assert torch.equal(b, eager_b[n]), ("due vs " + flush, n)
 
     restore()
