@@ -12,6 +12,21 @@
 
 namespace sk {
 
+// Loads of wave-uniform values through the scalar cache: the constant
+// address space tells the compiler that the memory does not change while
+// the kernel runs (the rank table and decay rates never do; the ring fills
+// are written by earlier launches), so a uniform address becomes an
+// s_load, which does not queue behind the vector loads of the waves already
+// in flight.
+typedef const __attribute__((address_space(4))) int const_int_t;
+typedef const __attribute__((address_space(4))) float const_float_t;
+__device__ __forceinline__ int uload(const int* base, int i) {
+  return ((const_int_t*)base)[i];     // (an address-space cast: C-style)
+}
+__device__ __forceinline__ float uload(const float* base, int i) {
+  return ((const_float_t*)base)[i];
+}
+
 // ---------------------------------------------------------------- Mamba-2
 // The read of a Mamba-2 layer is two launches.
 //
@@ -303,10 +318,36 @@ __global__ void __launch_bounds__(64 * M2R_WPB) m2_read_kernel(Params p) {
   const M2Work wl(p.B, p.R, p.G, W);
 
   // ------------------------------- ring fill (checked by the prep kernel)
-  const int n0c = reinterpret_cast<const int*>(reinterpret_cast<const float*>(p.work) + wl.n0)[bg];
-  const int off = p.off[h];
-  const int r = hv ? p.off[h + 1] - off : 0;
-  const float Ah = p.A[h];
+  // and the rank offsets and decay rates of the wave's heads, as scalars;
+  // each 16-lane row then takes its head's (heads past the group take the
+  // wave's first head, with no rows)
+  const int bgu = __builtin_amdgcn_readfirstlane(bgi);
+  const int n0c = uload(reinterpret_cast<const int*>(reinterpret_cast<const float*>(p.work) + wl.n0), bgu);
+  const int hb = __builtin_amdgcn_readfirstlane(g * HPG + wq * HPW);   // the wave's first head
+  int ob[HPW + 1];
+  float ab[HPW];
+#pragma unroll
+  for (int k = 0; k <= HPW; ++k) ob[k] = uload(p.off, min(hb + k, p.H));
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) ab[k] = uload(p.A, min(hb + k, p.H - 1));
+  // (all of them in flight at once and waited for together: the compiler
+  // would otherwise sink the offsets into the branch on the ring fill, a
+  // second round trip after the fill's)
+  asm volatile("" ::"s"(n0c));
+#pragma unroll
+  for (int k = 0; k <= HPW; ++k) asm volatile("" ::"s"(ob[k]));
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) asm volatile("" ::"s"(ab[k]));
+  int off = ob[0], offn = ob[1];
+  float Ah = ab[0];
+#pragma unroll
+  for (int k = 1; k < HPW; ++k) {
+    const bool me = hv && hh == k;
+    off = me ? ob[k] : off;
+    offn = me ? ob[k + 1] : offn;
+    Ah = me ? ab[k] : Ah;
+  }
+  const int r = hv ? offn - off : 0;
   const int n0 = n0c < 0 ? 0 : n0c;              // in range for every address below
   const int n = n0 + 1;
   __builtin_amdgcn_sched_barrier(0);
@@ -578,8 +619,8 @@ __global__ void __launch_bounds__(64 * DN_TPW) dn_read_kernel(Params p) {
 
   // the ring fill and the rank offsets first: every address below depends
   // on them, and the memory counter retires loads in order
-  const int n0raw = p.count[bh];
-  const int off = p.off[h], rk = p.off[h + 1] - off;
+  const int n0raw = uload(p.count, __builtin_amdgcn_readfirstlane((int)bh));   // (scalar loads)
+  const int off = uload(p.off, h), rk = uload(p.off, h + 1) - off;
   // the fixed map's rows of this head, staged through LDS once per workgroup
   // (two named registers, not an array: a private array would be placed in
   // LDS by the compiler, which then waits for the loads before issuing the
