@@ -503,11 +503,11 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2902285504,
+    "m2_b320": {"bytes": 2902274983,
                 "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
-    "gdn_b256": {"bytes": 1160797917,
+    "gdn_b256": {"bytes": 1160800775,
                  "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
-    "kda_b256": {"bytes": 1222504754,
+    "kda_b256": {"bytes": 1222487020,
                  "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
@@ -525,9 +525,9 @@ def timed_steps(k_req: int, window: int) -> int:
 # window's calls) from the same counter runs, with the digest of the read
 # kernels' sources at that time.
 TRAFFIC_READ = {
-    "m2_b320": {"bytes": 113286211, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
-    "gdn_b256": {"bytes": 62688329, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
-    "kda_b256": {"bytes": 98903509, "src_sha256": "85a9c37b18f648d1415bc3050a3b6a8d0834cd5d2bd8f260abad1ca325a26667"},
+    "m2_b320": {"bytes": 113357313, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
+    "gdn_b256": {"bytes": 62946681, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
+    "kda_b256": {"bytes": 99162644, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
 }
 READ_SOURCES = ("sk_read.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                 "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
