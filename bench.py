@@ -503,12 +503,12 @@ def main():
 # time the counters were taken.  A different digest means the kernel has
 # changed since, and the figure is reported as null.
 TRAFFIC = {
-    "m2_b320": {"bytes": 2902274983,
-                "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
-    "gdn_b256": {"bytes": 1160800775,
-                 "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
-    "kda_b256": {"bytes": 1222487020,
-                 "src_sha256": "4ce7d41b529690652976a093480ecaa7c1e1e9149156dba457c477610e2ac714"},
+    "m2_b320": {"bytes": 2902282922,
+                "src_sha256": "e1ee89e72ae57e1f55a04c5fb16f1cf495d3c16ed23417b55a529ed49b74fecc"},
+    "gdn_b256": {"bytes": 1160803639,
+                 "src_sha256": "e1ee89e72ae57e1f55a04c5fb16f1cf495d3c16ed23417b55a529ed49b74fecc"},
+    "kda_b256": {"bytes": 1222477881,
+                 "src_sha256": "e1ee89e72ae57e1f55a04c5fb16f1cf495d3c16ed23417b55a529ed49b74fecc"},
 }
 FLUSH_SOURCES = ("sk_tile.hpp", "sk_tile_body.inc", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                  "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")
@@ -525,9 +525,9 @@ def timed_steps(k_req: int, window: int) -> int:
 # window's calls) from the same counter runs, with the digest of the read
 # kernels' sources at that time.
 TRAFFIC_READ = {
-    "m2_b320": {"bytes": 113357313, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
-    "gdn_b256": {"bytes": 62946681, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
-    "kda_b256": {"bytes": 99162644, "src_sha256": "751bcd4e78f2d928f9dde0e39dd4d36a58c4faafea258b3d304bb1a935265781"},
+    "m2_b320": {"bytes": 113364584, "src_sha256": "94c78e460afb66aa8ab643aad06b5fc8ecc00f6d7ee781b8dd17b24d11f946cc"},
+    "gdn_b256": {"bytes": 62938981, "src_sha256": "94c78e460afb66aa8ab643aad06b5fc8ecc00f6d7ee781b8dd17b24d11f946cc"},
+    "kda_b256": {"bytes": 99139966, "src_sha256": "94c78e460afb66aa8ab643aad06b5fc8ecc00f6d7ee781b8dd17b24d11f946cc"},
 }
 READ_SOURCES = ("sk_read.hpp", "sk_device.hpp", "sk_params.hpp", "sk_dispatch.hpp",
                 "sk_m2.hip", "sk_gdn.hip", "sk_kda.hip")

@@ -12,21 +12,6 @@
 
 namespace sk {
 
-// Loads of wave-uniform values through the scalar cache: the constant
-// address space tells the compiler that the memory does not change while
-// the kernel runs (the rank table and decay rates never do; the ring fills
-// are written by earlier launches), so a uniform address becomes an
-// s_load, which does not queue behind the vector loads of the waves already
-// in flight.
-typedef const __attribute__((address_space(4))) int const_int_t;
-typedef const __attribute__((address_space(4))) float const_float_t;
-__device__ __forceinline__ int uload(const int* base, int i) {
-  return ((const_int_t*)base)[i];     // (an address-space cast: C-style)
-}
-__device__ __forceinline__ float uload(const float* base, int i) {
-  return ((const_float_t*)base)[i];
-}
-
 // ---------------------------------------------------------------- Mamba-2
 // The read of a Mamba-2 layer is two launches.
 //
