@@ -111,6 +111,17 @@ def test_m2_other_head_shapes(dk, dv, W):
     run(cfg, "sketch")
 
 
+@pytest.mark.parametrize("W", [16, 32])
+def test_m2_group_not_a_multiple_of_the_wave(W):
+    """Five heads per B/C group at the real head shape: the last read wave
+    of every group holds one head of the group (four heads a wave at W = 16,
+    two at W = 32) and lanes past it take no rows; every tile, ragged,
+    2W + 5 steps."""
+    cfg = CONFIGS["m2_b320"].with_(name=f"m2_hpg5_w{W}", heads=20, qk_groups=4, batch=3, window=W,
+                                   ragged=True, steps=2 * W + 5)
+    run(cfg, "sketch")
+
+
 @pytest.mark.parametrize("name", ["m2_b320", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("method", ["replay", "standard"])
 def test_small_batch_baselines(name, method):
